@@ -1,0 +1,218 @@
+"""Plain fp64 standard attention on the CPU (test infrastructure, see the package header).
+
+Notation follows the pages: S = scale * Q K^T, P = softmax(S) row by row,
+O = P V; m is a row's maximum score, l the sum of exp(S - m) over the row.
+The log-sum-exp LSE = m + ln(l) is the single statistic the library returns in
+place of the separate (l, m) pair that the [FA-notes] kernel sketch stores.
+
+Everything is computed in float64 from exactly-converted inputs; there is no
+tiling, fusion or reordering beyond row-blocking the query rows (rows of
+softmax are independent, so a row block is still the standard algorithm).
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import torch
+
+f64 = torch.float64
+
+
+def _as64(x) -> torch.Tensor:
+    if isinstance(x, torch.Tensor):
+        return x.detach().to("cpu").to(f64)
+    return torch.as_tensor(x, dtype=f64)
+
+
+def visible(i: int, j: int, Nq: int, Nk: int, causal: bool) -> bool:
+    """Causal visibility of key j from query row i.
+
+    [LLM-basics] ①-7 and ④-4: token i attends to tokens 1..i (itself and the
+    past).  The pages only state the square case; for Nq != Nk the rows are
+    aligned to the end of the key sequence (bottom-right), so key j is visible
+    iff j <= i + (Nk - Nq).  With Nq == Nk this is exactly the pages' rule, and
+    for a single decode query it means "every cached key".
+    """
+    return (not causal) or (j <= i + (Nk - Nq))
+
+
+def safe_softmax(x) -> torch.Tensor:
+    """Softmax along the last axis with the row maximum subtracted first.
+
+    [LLM-basics] ③-1: exp(x_i - m) / sum_j exp(x_j - m) equals the plain
+    softmax because the common factor exp(-m) cancels; subtracting the maximum
+    keeps every exponent <= 0 so nothing overflows.  [FA-notes] §5.1 shows the
+    same three steps (max, exp of the shifted row, divide by the sum).
+    Entries equal to -inf (masked) get probability exactly 0.
+    """
+    x = _as64(x)
+    m = torch.amax(x, dim=-1, keepdim=True)
+    e = torch.exp(x - m)
+    return e / torch.sum(e, dim=-1, keepdim=True)
+
+
+def _scores(q_rows: torch.Tensor, k: torch.Tensor, scale: float, row0: int, Nq: int,
+            causal: bool) -> torch.Tensor:
+    """S = scale * Q K^T for query rows [row0, row0 + len) with the causal mask applied.
+
+    [LLM-basics] ①-2 steps 1-2 (dot products, then divide by sqrt(d_k));
+    masked entries are set to -inf ([LLM-basics] ④-4: future positions filled
+    with negative infinity so softmax gives them exactly zero weight).
+    """
+    s = (q_rows @ k.transpose(0, 1)) * scale
+    if causal:
+        Nk = k.shape[0]
+        rows = torch.arange(row0, row0 + q_rows.shape[0]).unsqueeze(1)
+        cols = torch.arange(Nk).unsqueeze(0)
+        s = s.masked_fill(cols > rows + (Nk - Nq), float("-inf"))
+    return s
+
+
+def attention(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None,
+              heads: Optional[Sequence[int]] = None,
+              rows: Optional[Tuple[int, int]] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Standard attention, materialising S and P per (batch, head).
+
+    q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] (any float dtype, converted exactly
+    to fp64).  Returns O [B, Nq, Hq, d] and LSE [B, Hq, Nq] in float64.
+
+    Steps, in the order of [LLM-basics] ①-2 and [FA-evo] "표준 Attention 연산 과정":
+      1. S = scale * Q K^T (scale is the caller's, 1/sqrt(d) for the workloads);
+      2. causal mask (see ``visible``);
+      3. m = row max; E = exp(S - m); l = row sum of E; P = E / l  (safe softmax);
+      4. O = P V;  LSE = m + ln(l).
+    GQA ([LLM-basics] ②-7): Hq/Hkv consecutive query heads share one K/V head,
+    kvh = h // (Hq // Hkv).
+
+    ``heads`` restricts the work to some query heads and ``rows`` to a query-row
+    range [r0, r1); entries outside are left as NaN.  ``row_block`` bounds the
+    memory of S and P by processing that many query rows at a time.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    group = Hq // Hkv
+    o = torch.full((B, Nq, Hq, d), float("nan"), dtype=f64)
+    lse = torch.full((B, Hq, Nq), float("nan"), dtype=f64)
+    r0, r1 = rows if rows is not None else (0, Nq)
+    step = row_block or (r1 - r0)
+    for b in range(B):
+        for h in (heads if heads is not None else range(Hq)):
+            kvh = h // group
+            kk = k[b, :, kvh, :]
+            vv = v[b, :, kvh, :]
+            for a in range(r0, r1, step):
+                e_ = min(a + step, r1)
+                s = _scores(q[b, a:e_, h, :], kk, scale, a, Nq, causal)
+                m = torch.amax(s, dim=1, keepdim=True)
+                ex = torch.exp(s - m)
+                l = torch.sum(ex, dim=1, keepdim=True)
+                p = ex / l
+                o[b, a:e_, h, :] = p @ vv
+                lse[b, h, a:e_] = (m + torch.log(l)).squeeze(1)
+    return o, lse
+
+
+def attention_probs(q, k, v, scale: float, causal: bool, b: int = 0, h: int = 0) -> torch.Tensor:
+    """The probability matrix P [Nq, Nk] of one (batch, head), for invariant checks."""
+    q, k = _as64(q), _as64(k)
+    Hq, Hkv = q.shape[2], k.shape[2]
+    kvh = h // (Hq // Hkv)
+    s = _scores(q[b, :, h, :], k[b, :, kvh, :], scale, 0, q.shape[1], causal)
+    return safe_softmax(s)
+
+
+def decode_attention(q, k_cache, v_cache, lengths, scale: float,
+                     heads: Optional[Sequence[int]] = None,
+                     batches: Optional[Iterable[int]] = None):
+    """One decode step: q [B, Hq, d] against the first lengths[b] rows of the cache.
+
+    [LLM-basics] ②-3 / ②-4: the new token's query attends to every cached key
+    and value of its sequence (the cache is read whole each step).  It is the
+    same standard attention with Nq = 1 and Nk = lengths[b] (all keys visible);
+    the cache rows at or beyond lengths[b] are never read.  Returns O [B, Hq, d]
+    and LSE [B, Hq] in float64 (NaN where a head or batch was not requested).
+    """
+    q = _as64(q)
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    o = torch.full((B, Hq, d), float("nan"), dtype=f64)
+    lse = torch.full((B, Hq), float("nan"), dtype=f64)
+    hs = list(heads) if heads is not None else list(range(Hq))
+    for b in (batches if batches is not None else range(B)):
+        L = int(lengths[b])
+        kk = _as64(k_cache[b, :L])          # [L, Hkv, d]
+        vv = _as64(v_cache[b, :L])
+        oo, ll = attention(q[b].reshape(1, 1, Hq, d), kk.unsqueeze(0), vv.unsqueeze(0), scale,
+                           causal=False, heads=hs)
+        o[b, hs] = oo[0, 0, hs]
+        lse[b, hs] = ll[0, hs, 0]
+    return o, lse
+
+
+def online_softmax_update(m_prev: torch.Tensor, l_prev: torch.Tensor, acc_prev: torch.Tensor,
+                          s_block: torch.Tensor, v_block: torch.Tensor):
+    """One block step of the online softmax, per row.
+
+    [FA-notes] §4 and [LLM-basics] ③-2: with the running maximum m_prev and
+    running sum l_prev, a new block of scores with maximum m_cur gives
+        m_new = max(m_prev, m_cur)
+        l_new = e^(m_prev - m_new) * l_prev + e^(m_cur - m_new) * l_cur,
+    where l_cur = sum exp(s_block - m_cur).  [FA-notes] §5.2 rescales the
+    unnormalised output the same way:
+        acc_new = e^(m_prev - m_new) * acc_prev + e^(m_cur - m_new) * exp(s_block - m_cur) V_block.
+    m_prev = -inf, l_prev = 0, acc_prev = 0 before the first block (the sketch
+    leaves these uninitialised; this is the reading that makes the first step
+    reduce to the block's own softmax numerator).  Rows are the leading axis.
+    """
+    s_block = _as64(s_block)
+    m_cur = torch.amax(s_block, dim=-1)
+    p_cur = torch.exp(s_block - m_cur.unsqueeze(-1))
+    l_cur = torch.sum(p_cur, dim=-1)
+    m_new = torch.maximum(m_prev, m_cur)
+    alpha = torch.exp(m_prev - m_new)
+    beta = torch.exp(m_cur - m_new)
+    l_new = alpha * l_prev + beta * l_cur
+    acc_new = alpha.unsqueeze(-1) * acc_prev + (beta.unsqueeze(-1) * p_cur) @ _as64(v_block)
+    return m_new, l_new, acc_new
+
+
+def online_attention_rows(s: torch.Tensor, v: torch.Tensor, block_edges: List[int]):
+    """Attention of score rows s [R, N] with values v [N, dv], consuming the keys in the
+    contiguous blocks [e0, e1), [e1, e2), ... given by ``block_edges`` (e0 = 0,
+    last = N), via ``online_softmax_update``; the final output is acc / l
+    ([FA-notes] §5.2: P = exp(S - m) / l).  Returns (O, LSE) with LSE = m + ln l.
+    """
+    s, v = _as64(s), _as64(v)
+    R = s.shape[0]
+    m = torch.full((R,), float("-inf"), dtype=f64)
+    l = torch.zeros((R,), dtype=f64)
+    acc = torch.zeros((R, v.shape[1]), dtype=f64)
+    for a, e in zip(block_edges[:-1], block_edges[1:]):
+        m, l, acc = online_softmax_update(m, l, acc, s[:, a:e], v[a:e])
+    return acc / l.unsqueeze(-1), m + torch.log(l)
+
+
+def lse_merge(o_parts, lse_parts) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Combine per-chunk normalised outputs O_c and log-sum-exps lse_c of one row.
+
+    This is the [FA-notes] §4 two-block merge applied to any number of blocks,
+    written with LSE in place of (m, l): each chunk's l_c = e^(lse_c - M) up to
+    the common factor e^M with M = max_c lse_c, so
+        LSE = M + ln sum_c e^(lse_c - M),   O = sum_c e^(lse_c - LSE) O_c.
+    o_parts: [C, ..., dv]; lse_parts: [C, ...].
+    """
+    o_parts, lse_parts = _as64(o_parts), _as64(lse_parts)
+    M = torch.amax(lse_parts, dim=0)
+    w = torch.exp(lse_parts - M)
+    lse = M + torch.log(torch.sum(w, dim=0))
+    wn = torch.exp(lse_parts - lse)
+    o = torch.sum(wn.unsqueeze(-1) * o_parts, dim=0)
+    return o, lse
+
+
+def log_sum_exp_scalar(xs: Sequence[float]) -> float:
+    """ln sum_i e^{x_i} for a short Python list (used by the brute-force pins)."""
+    m = max(xs)
+    return m + math.log(sum(math.exp(x - m) for x in xs))

@@ -1,0 +1,428 @@
+"""Pins of the fp64 oracle to facts other than itself.
+
+Each ``pin_*`` function takes an oracle-like module (the real ``oracle`` or a
+copy with a planted mistake) and raises AssertionError when the module
+disagrees with what the pages or the mathematics fix.  ``test_oracle.py`` runs
+them on the real oracle; ``test_oracle_mutants.py`` runs them on mutated copies
+and requires every planted mistake to be caught by at least one pin.
+
+Page titles (cited by section below):
+  [FA-notes]   "flash-attn" notes, minjae-portfolio.vercel.app/notes/flash-attn
+  [LLM-basics] "LLM 기초 — Attention부터 FlashAttention까지", gylee815.github.io/llmso/w1
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+f64 = torch.float64
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _close(a, b, tol, what=""):
+    a = torch.as_tensor(a, dtype=f64)
+    b = torch.as_tensor(b, dtype=f64)
+    err = (a - b).abs().max().item() if a.numel() else 0.0
+    assert a.shape == b.shape, f"{what}: shape {tuple(a.shape)} vs {tuple(b.shape)}"
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def _rand(shape, seed, scale=1.0):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=f64) * scale
+
+
+def _example_tensors():
+    ex = _golden("worked_example.json")
+    q = torch.tensor(ex["query"], dtype=f64).reshape(1, 1, 1, 2)
+    k = torch.tensor(ex["keys"], dtype=f64).reshape(1, 3, 1, 2)
+    v = torch.tensor(ex["values"], dtype=f64).reshape(1, 3, 1, 2)
+    return ex, q, k, v
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked numbers
+# ---------------------------------------------------------------------------
+
+def pin_worked_example_printed(orc):
+    """[LLM-basics] ①-2 worked example: the page's printed numbers, at the page's rounding."""
+    ex, q, k, v = _example_tensors()
+    scale = 1.0 / math.sqrt(ex["d_k"])
+    o, lse = orc.attention(q, k, v, scale, causal=False)
+    p = orc.attention_probs(q, k, v, scale, causal=False)[0]
+    pr, dec = ex["printed"], ex["printed_decimals"]
+
+    def at(x, key):
+        _close(x, pr[key], 0.5 * 10 ** (-dec[key]) + 1e-12, f"worked example {key}")
+
+    # scaled scores: LSE - ln p_j recovers s_j for every key (s_j = LSE + ln P_j)
+    s = lse[0, 0, 0] + torch.log(p)
+    at(s, "scaled_scores")
+    at(s * math.sqrt(ex["d_k"]), "raw_scores")
+    at(torch.exp(s), "exp_scaled")
+    at(torch.exp(lse[0, 0, 0]), "exp_sum")   # sum_j e^{s_j} since no shift is needed here
+    at(p, "softmax")
+    at(o[0, 0, 0], "output")
+
+
+def pin_worked_example_closed_form(orc):
+    """Same example, exact: with a = e^{1/sqrt 2}, P = [a, 1, a]/(2a+1),
+    O = [2a, a + 2]/(2a+1), LSE = ln(2a+1)."""
+    ex, q, k, v = _example_tensors()
+    a = math.exp(1.0 / math.sqrt(2.0))
+    den = 2 * a + 1
+    o, lse = orc.attention(q, k, v, 1.0 / math.sqrt(2.0), causal=False)
+    p = orc.attention_probs(q, k, v, 1.0 / math.sqrt(2.0), causal=False)[0]
+    _close(p, [a / den, 1 / den, a / den], 1e-15, "closed-form P")
+    _close(o[0, 0, 0], [2 * a / den, (a + 2) / den], 1e-15, "closed-form O")
+    _close(lse[0, 0, 0], math.log(den), 1e-15, "closed-form LSE")
+
+
+def pin_softmax_examples(orc):
+    """[LLM-basics] ①-3: softmax([1,2]) ~ [0.27, 0.73], softmax([10,20]) ~ [0.00005, 0.99995];
+    exactly [1, e]/(1+e) and [1, e^10]/(1+e^10)."""
+    g = _golden("softmax_examples.json")
+    for case in g["cases"]:
+        got = orc.safe_softmax(torch.tensor(case["x"], dtype=f64))
+        _close(got, case["printed"], 0.5 * 10 ** (-case["decimals"]) + 1e-12, f"softmax {case['x']}")
+        d = case["x"][1] - case["x"][0]
+        exact = [1 / (1 + math.exp(d)), math.exp(d) / (1 + math.exp(d))]
+        _close(got, exact, 1e-15, f"softmax closed form {case['x']}")
+
+
+def pin_overflow(orc):
+    """[LLM-basics] ③-1: exp overflows fp16 near x = 11.1 and fp32 near x = 88.7 (page's
+    table), and a score of 100 already overflows fp32; the safe (max-subtracted)
+    softmax stays finite and exact.  In fp64 the same holds at 1000 > ln(DBL_MAX)."""
+    g = _golden("overflow_thresholds.json")
+    for row in g["rows"]:
+        fmax = float(np.finfo(getattr(np, row["dtype"])).max)
+        assert abs(fmax - row["max_printed"]) <= 0.01 * row["max_printed"]
+        assert round(math.log(fmax), row["x_decimals"]) == row["overflow_x_printed"]
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.exp(np.float32(g["example_score"])))
+    for big in (g["example_score"], 1000.0):
+        x = torch.tensor([big, big - 1.0, 0.0], dtype=f64)
+        got = orc.safe_softmax(x)
+        assert torch.isfinite(got).all(), f"safe softmax not finite at {big}"
+        e1 = math.exp(-1.0)
+        den = 1 + e1 + math.exp(-big)
+        _close(got, [1 / den, e1 / den, math.exp(-big) / den], 1e-15, f"softmax at {big}")
+    # attention whose scores reach ~1000: finite, LSE = max score + ln(sum of shifted exps)
+    q = torch.tensor([[[[10.0, 0.0]]]], dtype=f64)
+    k = torch.tensor([[[[100.0, 0.0]], [[99.9, 0.0]]]], dtype=f64)
+    v = torch.tensor([[[[1.0, -1.0]], [[3.0, 5.0]]]], dtype=f64)
+    o, lse = orc.attention(q, k, v, 1.0, causal=False)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    w = math.exp(-1.0)
+    _close(lse[0, 0, 0], 1000.0 + math.log(1 + w), 1e-12, "LSE at score 1000")
+    _close(o[0, 0, 0], [(1 + 3 * w) / (1 + w), (-1 + 5 * w) / (1 + w)], 1e-14, "O at score 1000")
+
+
+def pin_causal_visibility(orc):
+    """[LLM-basics] ①-7 / ④-4: with five tokens, token n (1-based) sees tokens 1..n."""
+    g = _golden("causal_visibility.json")
+    n = g["tokens"]
+    for i in range(n):
+        seen = [j + 1 for j in range(n) if orc.visible(i, j, n, n, True)]
+        assert seen == g["visible_1based"][str(i + 1)], f"row {i + 1}: {seen}"
+    # the same through the probability matrix: masked weights are exactly zero
+    q, k, v = _rand((1, n, 1, 4), 1), _rand((1, n, 1, 4), 2), _rand((1, n, 1, 4), 3)
+    p = orc.attention_probs(q, k, v, 0.5, causal=True)
+    for i in range(n):
+        vis = [j + 1 for j in range(n) if p[i, j] > 0]
+        assert vis == g["visible_1based"][str(i + 1)], f"P row {i + 1}: {vis}"
+
+
+# ---------------------------------------------------------------------------
+# invariants that hold at any size
+# ---------------------------------------------------------------------------
+
+_SHAPES = [  # B, Nq, Nk, Hq, Hkv, d, causal
+    (1, 37, 37, 2, 2, 8, True),
+    (2, 19, 45, 4, 2, 16, True),
+    (1, 23, 31, 3, 1, 8, False),
+]
+
+
+def _qkv(shape, seed, gain=1.0):
+    B, Nq, Nk, Hq, Hkv, d, _ = shape
+    return (_rand((B, Nq, Hq, d), seed, gain), _rand((B, Nk, Hkv, d), seed + 1, gain),
+            _rand((B, Nk, Hkv, d), seed + 2))
+
+
+def pin_rows_sum_to_one(orc):
+    """Every row of P is a probability distribution ([LLM-basics] ①-2 step 3, ③-1)."""
+    for t, shape in enumerate(_SHAPES):
+        q, k, v = _qkv(shape, 10 * t)
+        for h in range(shape[3]):
+            p = orc.attention_probs(q, k, v, 0.3, shape[6], b=0, h=h)
+            assert (p >= 0).all()
+            _close(p.sum(dim=1), torch.ones(p.shape[0], dtype=f64), 1e-12, "row sums")
+
+
+def pin_constant_v(orc):
+    """V_j = c for every key j  =>  O_i = c for every row (weights sum to one)."""
+    for t, shape in enumerate(_SHAPES):
+        B, Nq, Nk, Hq, Hkv, d, causal = shape
+        q, k, _ = _qkv(shape, 20 * t)
+        c = _rand((B, 1, Hkv, d), 99)
+        v = c.expand(B, Nk, Hkv, d).clone()
+        o, _ = orc.attention(q, k, v, 0.4, causal)
+        want = torch.repeat_interleave(c, Hq // Hkv, dim=2).expand(B, Nq, Hq, d)
+        _close(o, want, 1e-13, "constant V")
+
+
+def pin_dominant_score(orc):
+    """One key whose score exceeds every other visible score by >= 50 takes all the
+    weight: O_i = V_j up to e^-50 ([LLM-basics] ①-3's [10,20] example taken to the limit)."""
+    Nq = Nk = 16
+    d = 4
+    q = torch.zeros((1, Nq, 1, d), dtype=f64)
+    q[..., 0] = 1.0
+    k = _rand((1, Nk, 1, d), 5, 0.1)
+    k[..., 0] = 0.0
+    star = 3
+    k[0, star, 0, 0] = 60.0
+    v = _rand((1, Nk, 1, d), 6)
+    o, lse = orc.attention(q, k, v, 1.0, causal=False)
+    _close(o[0, :, 0, :], v[0, star, 0, :].expand(Nq, d), 1e-15 + 20 * math.exp(-50), "dominant key")
+    # causal: rows before the dominant key cannot see it
+    o2, _ = orc.attention(q, k, v, 1.0, causal=True)
+    _close(o2[0, star:, 0, :], v[0, star, 0, :].expand(Nq - star, d), 1e-15 + 20 * math.exp(-50),
+           "dominant key, causal")
+    assert (o2[0, :star, 0, :] - v[0, star, 0, :]).abs().max() > 1e-3
+
+
+def pin_causal_row0(orc):
+    """Causal, Nq = Nk: row 0 sees only key 0, so O_0 = V_0 and LSE_0 = scale * q_0 . k_0."""
+    for t, shape in enumerate(_SHAPES[:1]):
+        B, Nq, Nk, Hq, Hkv, d, _ = shape
+        q, k, v = _qkv(shape, 30)
+        o, lse = orc.attention(q, k, v, 0.7, causal=True)
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            _close(o[0, 0, h], v[0, 0, kvh], 0.0, "row 0 = V[0]")
+            _close(lse[0, h, 0], 0.7 * float((q[0, 0, h] * k[0, 0, kvh]).sum()), 1e-14, "LSE_0")
+
+
+def pin_uniform_closed_form(orc):
+    """K = 0 makes every visible score 0: causal O_i = mean(V_0..V_{i+Nk-Nq}) with
+    LSE_i = ln(i + Nk - Nq + 1); non-causal O_i = mean(V), LSE_i = ln Nk."""
+    for (Nq, Nk) in ((12, 12), (5, 17)):
+        q = _rand((1, Nq, 2, 6), 40)
+        k = torch.zeros((1, Nk, 1, 6), dtype=f64)
+        v = _rand((1, Nk, 1, 6), 41)
+        o, lse = orc.attention(q, k, v, 0.125, causal=True)
+        for i in range(Nq):
+            last = i + Nk - Nq
+            for h in range(2):
+                _close(o[0, i, h], v[0, :last + 1, 0].mean(dim=0), 1e-15, "uniform causal O")
+                _close(lse[0, h, i], math.log(last + 1), 1e-15, "uniform causal LSE")
+        o, lse = orc.attention(q, k, v, 0.125, causal=False)
+        _close(o[0, :, 0], v[0, :, 0].mean(dim=0).expand(Nq, 6), 1e-15, "uniform O")
+        _close(lse, torch.full((1, 2, Nq), math.log(Nk), dtype=f64), 1e-15, "uniform LSE")
+
+
+def pin_gqa_repeat(orc):
+    """[LLM-basics] ②-7: 14 query heads share 2 K/V heads in groups of 7.  Equal to
+    MHA over K/V heads repeated 7 times consecutively."""
+    g = _golden("gqa_example.json")
+    Hq, Hkv, d = g["num_attention_heads"], g["num_key_value_heads"], 8
+    assert Hq // Hkv == g["num_key_value_groups"]
+    q, k, v = _rand((1, 9, Hq, d), 50), _rand((1, 9, Hkv, d), 51), _rand((1, 9, Hkv, d), 52)
+    o, lse = orc.attention(q, k, v, 0.3, causal=True)
+    kr = torch.repeat_interleave(k, Hq // Hkv, dim=2)
+    vr = torch.repeat_interleave(v, Hq // Hkv, dim=2)
+    o2, lse2 = orc.attention(q, kr, vr, 0.3, causal=True)
+    _close(o, o2, 0.0, "GQA O")
+    _close(lse, lse2, 0.0, "GQA LSE")
+    # and head h really uses K/V head h // 7 (not h % 2): compare one head by hand
+    for h in (0, 6, 7, 13):
+        oh, lh = orc.attention(q[:, :, h:h + 1], k[:, :, h // 7:h // 7 + 1], v[:, :, h // 7:h // 7 + 1],
+                               0.3, causal=True)
+        _close(o[:, :, h], oh[:, :, 0], 0.0, f"GQA head {h}")
+
+
+def pin_key_permutation(orc):
+    """Non-causal attention is a function of the set of (key, value) pairs: permuting
+    them jointly leaves O and LSE unchanged."""
+    shape = _SHAPES[2]
+    q, k, v = _qkv(shape, 60)
+    perm = torch.randperm(shape[2], generator=torch.Generator().manual_seed(61))
+    o, lse = orc.attention(q, k, v, 0.3, causal=False)
+    o2, lse2 = orc.attention(q, k[:, perm], v[:, perm], 0.3, causal=False)
+    _close(o, o2, 1e-14, "permuted O")
+    _close(lse, lse2, 1e-14, "permuted LSE")
+
+
+# ---------------------------------------------------------------------------
+# the online softmax merge, brute-forced
+# ---------------------------------------------------------------------------
+
+def _compositions(n):
+    """All ways to cut range(n) into contiguous non-empty blocks, as edge lists."""
+    for cuts in itertools.product((0, 1), repeat=n - 1):
+        edges = [0] + [i + 1 for i, c in enumerate(cuts) if c] + [n]
+        yield edges
+
+
+def pin_online_merge_bruteforce(orc):
+    """[FA-notes] §4 / §5.2, [LLM-basics] ③-2: block-by-block online softmax with output
+    rescaling equals the one-shot softmax for EVERY split of a row into contiguous
+    blocks (rows of length 1..8, all 2^(n-1) splits)."""
+    for n in range(1, 9):
+        s = _rand((3, n), 70 + n, 3.0)
+        s[1, n // 2] = 40.0             # a late large score forces a max change
+        v = _rand((n, 5), 80 + n)
+        p = torch.exp(s - s.max(dim=1, keepdim=True).values)
+        o_ref = (p / p.sum(dim=1, keepdim=True)) @ v
+        lse_ref = torch.logsumexp(s, dim=1)
+        for edges in _compositions(n):
+            o, lse = orc.online_attention_rows(s, v, edges)
+            _close(o, o_ref, 1e-14, f"online O n={n} edges={edges}")
+            _close(lse, lse_ref, 1e-14, f"online LSE n={n} edges={edges}")
+    # a single update step reproduces the pages' two-block formulas on scalars
+    m1, l1, m2 = 1.5, 2.0, 3.0
+    x2 = torch.tensor([[3.0, 2.0]], dtype=f64)
+    l2 = math.exp(0.0) + math.exp(-1.0)
+    m, l, acc = orc.online_softmax_update(torch.tensor([m1], dtype=f64), torch.tensor([l1], dtype=f64),
+                                          torch.zeros((1, 1), dtype=f64), x2,
+                                          torch.ones((2, 1), dtype=f64))
+    _close(m, [3.0], 0.0, "m_new = max(m1, m2)")
+    _close(l, [math.exp(m1 - 3.0) * l1 + math.exp(m2 - 3.0) * l2], 1e-15, "l_new")
+    _close(acc, [[l2]], 1e-15, "acc with V = 1 equals the block's exp sum")
+
+
+def pin_lse_merge_decode(orc):
+    """Splitting one decode row's keys into 256-key chunks, attending to each chunk and
+    merging the (O_c, lse_c) pairs gives the unsplit result (the two-block merge of
+    [FA-notes] §4 applied across chunks)."""
+    for L in (1, 255, 256, 257, 700):
+        q = _rand((1, 1, 2, 8), 90 + L)
+        k = _rand((1, L, 1, 8), 91 + L, 2.0)
+        v = _rand((1, L, 1, 8), 92 + L)
+        o_ref, lse_ref = orc.attention(q, k, v, 0.35, causal=False)
+        parts_o, parts_l = [], []
+        for a in range(0, L, 256):
+            oc, lc = orc.attention(q, k[:, a:a + 256], v[:, a:a + 256], 0.35, causal=False)
+            parts_o.append(oc[0, 0])
+            parts_l.append(lc[0, :, 0])
+        o, lse = orc.lse_merge(torch.stack(parts_o), torch.stack(parts_l))
+        _close(o, o_ref[0, 0], 1e-14, f"merged O L={L}")
+        _close(lse, lse_ref[0, :, 0], 1e-14, f"merged LSE L={L}")
+
+
+def pin_decode_matches_prefill(orc):
+    """Decode = the same attention with one query row over the first L_b cache rows;
+    cache rows beyond L_b (NaN) are never touched."""
+    B, Hq, Hkv, d, Nmax = 3, 4, 2, 8, 40
+    lengths = [1, 17, 40]
+    q = _rand((B, Hq, d), 100)
+    kc = _rand((B, Nmax, Hkv, d), 101)
+    vc = _rand((B, Nmax, Hkv, d), 102)
+    for b, L in enumerate(lengths):
+        kc[b, L:] = float("nan")
+        vc[b, L:] = float("nan")
+    o, lse = orc.decode_attention(q, kc, vc, lengths, 0.25)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    for b, L in enumerate(lengths):
+        o2, l2 = orc.attention(q[b].reshape(1, 1, Hq, d), kc[b:b + 1, :L], vc[b:b + 1, :L], 0.25,
+                               causal=True)
+        _close(o[b], o2[0, 0], 0.0, "decode O")
+        _close(lse[b], l2[0, :, 0], 0.0, "decode LSE")
+    # L = 1: the single cached value, LSE = its score
+    _close(o[0], vc[0, 0].repeat_interleave(Hq // Hkv, dim=0), 0.0, "L=1 decode")
+
+
+# ---------------------------------------------------------------------------
+# independent re-computations
+# ---------------------------------------------------------------------------
+
+def pin_bruteforce_loops(orc):
+    """Tiny shapes against scalar Python loops written from the definition
+    (dot products, mask, max, exp, sum, weighted sum), both causal alignments."""
+    for (B, Nq, Nk, Hq, Hkv, d, causal) in ((2, 3, 5, 4, 2, 3, True), (1, 4, 4, 2, 1, 2, True),
+                                            (1, 3, 2, 3, 3, 2, False)):
+        q = _rand((B, Nq, Hq, d), 110)
+        k = _rand((B, Nk, Hkv, d), 111)
+        v = _rand((B, Nk, Hkv, d), 112)
+        scale = 0.6
+        o, lse = orc.attention(q, k, v, scale, causal)
+        ql, kl, vl = q.tolist(), k.tolist(), v.tolist()
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                g = h // G
+                for i in range(Nq):
+                    sc = []
+                    for j in range(Nk):
+                        if causal and j > i + (Nk - Nq):
+                            continue
+                        sc.append((j, scale * sum(ql[b][i][h][c] * kl[b][j][g][c] for c in range(d))))
+                    mx = max(s for _, s in sc)
+                    w = [(j, math.exp(s - mx)) for j, s in sc]
+                    tot = sum(x for _, x in w)
+                    for c in range(d):
+                        want = sum(x * vl[b][j][g][c] for j, x in w) / tot
+                        assert abs(o[b, i, h, c].item() - want) < 1e-13, (b, i, h, c)
+                    assert abs(lse[b, h, i].item() - (mx + math.log(tot))) < 1e-13
+
+
+def pin_sdpa_crosscheck(orc):
+    """A library routine: torch's scaled_dot_product_attention on the CPU in fp64
+    ([FA-notes] §6 names it as where FlashAttention is used), K/V heads repeated
+    for GQA; LSE against torch.logsumexp of the masked scores."""
+    import torch.nn.functional as F
+    for (B, Nq, Nk, Hq, Hkv, d, causal) in ((1, 128, 128, 1, 1, 64, False), (2, 64, 64, 4, 2, 16, True),
+                                            (1, 33, 70, 4, 1, 16, True)):
+        q = _rand((B, Nq, Hq, d), 120)
+        k = _rand((B, Nk, Hkv, d), 121)
+        v = _rand((B, Nk, Hkv, d), 122)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = orc.attention(q, k, v, scale, causal)
+        qt = q.permute(0, 2, 1, 3)
+        kt = torch.repeat_interleave(k, Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+        vt = torch.repeat_interleave(v, Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+        mask = None
+        if causal:
+            i = torch.arange(Nq).unsqueeze(1)
+            j = torch.arange(Nk).unsqueeze(0)
+            mask = j <= i + (Nk - Nq)
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+        _close(o.permute(0, 2, 1, 3), ref, 1e-12, "SDPA O")
+        s = (qt @ kt.transpose(-1, -2)) * scale
+        if mask is not None:
+            s = s.masked_fill(~mask, float("-inf"))
+        _close(lse, torch.logsumexp(s, dim=-1), 1e-12, "logsumexp LSE")
+
+
+ALL_PINS = [
+    pin_worked_example_printed,
+    pin_worked_example_closed_form,
+    pin_softmax_examples,
+    pin_overflow,
+    pin_causal_visibility,
+    pin_rows_sum_to_one,
+    pin_constant_v,
+    pin_dominant_score,
+    pin_causal_row0,
+    pin_uniform_closed_form,
+    pin_gqa_repeat,
+    pin_key_permutation,
+    pin_online_merge_bruteforce,
+    pin_lse_merge_decode,
+    pin_decode_matches_prefill,
+    pin_bruteforce_loops,
+    pin_sdpa_crosscheck,
+]

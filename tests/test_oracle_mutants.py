@@ -1,0 +1,62 @@
+"""Plant plausible mistakes in copies of the oracle and require the pins to catch each.
+
+Each mutant is the oracle's own source with one textual change (a dropped term,
+a wrong sign, index, axis or operand), loaded as a separate module on the CPU.
+A mutant "survives" if every pin still passes; no mutant may survive.
+"""
+import importlib.util
+import os
+import sys
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "attention.py")
+
+MUTANTS = {
+    "scale dropped": ("s = (q_rows @ k.transpose(0, 1)) * scale", "s = (q_rows @ k.transpose(0, 1))"),
+    "mask off by one": ("cols > rows + (Nk - Nq)", "cols >= rows + (Nk - Nq)"),
+    "mask top-left": ("cols > rows + (Nk - Nq)", "cols > rows"),
+    "visible off by one": ("(j <= i + (Nk - Nq))", "(j < i + (Nk - Nq))"),
+    "gqa modulo": ("kvh = h // group", "kvh = h % Hkv"),
+    "lse without ln l": ("(m + torch.log(l)).squeeze(1)", "m.squeeze(1)"),
+    "wrong value operand": ("o[b, a:e_, h, :] = p @ vv", "o[b, a:e_, h, :] = p @ kk"),
+    "max over wrong axis": ("m = torch.amax(s, dim=1, keepdim=True)",
+                            "m = torch.amax(s, dim=0, keepdim=True)"),
+    "sum over wrong axis": ("l = torch.sum(ex, dim=1, keepdim=True)",
+                            "l = torch.sum(ex, dim=0, keepdim=True)"),
+    "no max shift in attention": ("ex = torch.exp(s - m)", "ex = torch.exp(s)"),
+    "softmax without max shift": ("e = torch.exp(x - m)", "e = torch.exp(x)"),
+    "alpha sign": ("alpha = torch.exp(m_prev - m_new)", "alpha = torch.exp(m_new - m_prev)"),
+    "beta dropped on acc": ("(beta.unsqueeze(-1) * p_cur) @", "(p_cur) @"),
+    "l_new misses beta": ("l_new = alpha * l_prev + beta * l_cur", "l_new = alpha * l_prev + l_cur"),
+    "merge weight vs M": ("wn = torch.exp(lse_parts - lse)", "wn = torch.exp(lse_parts - M)"),
+    "final O not normalised": ("return acc / l.unsqueeze(-1), m + torch.log(l)",
+                               "return acc, m + torch.log(l)"),
+    "decode reads one row short": ("L = int(lengths[b])", "L = max(int(lengths[b]) - 1, 1)"),
+    "decode reads past length": ("kk = _as64(k_cache[b, :L])", "kk = _as64(k_cache[b, :L + 1])"),
+}
+
+
+def _load_mutant(name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name!r} not unique/found"
+    mod = types.ModuleType(f"oracle_mutant_{abs(hash(name))}")
+    mod.__file__ = SRC
+    exec(compile(src.replace(old, new), SRC, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _load_mutant(name, *MUTANTS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # AssertionError, or the mutant crashing on a shape
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name!r} passed every pin"

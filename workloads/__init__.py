@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU parity tests and bench.py.
+
+This module holds the workload table and the random-input recipe only.  It does
+no attention arithmetic of any kind: it draws normal variates, rounds them to
+the storage dtype and (for decode) poisons the unused cache rows with NaN.
+
+Recipe (the pages give shapes but no generator, so this is a stated choice):
+  * one ``torch.Generator('cpu')`` seeded with ``seed`` (0 for every workload);
+  * prefill draws Q, then K, then V as fp32 ``randn`` in the [B, N, H, d] layout;
+    the "peaky" workload multiplies Q and K by 1.5 in fp32; bf16 workloads then
+    round to bfloat16 (round-to-nearest-even, torch's conversion);
+  * decode draws the per-sequence key counts first (``randint(lo, hi + 1)``,
+    both ends inclusive), then q [B, Hq, d], then the K cache and the V cache
+    [B, Nk_max, Hkv, d]; cache rows at or beyond a sequence's length are set to
+    NaN so that any read of them shows up in the result.
+
+Shapes follow the pages' workloads: the packed-QKV usage example of the
+"Attention is All You Need부터 FlashAttention-3까지" page (section "실전 구현")
+is B=2, S=2048, H=12, D=64; the d=128 / GQA-8 long-context shapes stand in for
+the Llama-class 32K-context runs that page quotes (section "실무 활용"); the
+decode workload follows the KV-cache / GQA sections (②-3, ②-7) of
+"LLM 기초 — Attention부터 FlashAttention까지".  No dataset is involved.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    workload: str           # human-readable description with sizes
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    dtype: str              # "f32" or "bf16"
+    qk_gain: float = 1.0    # Q and K multiplied by this before rounding
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs: 4*B*Hq*Nq*Nk*d, halved when causal."""
+        f = 4.0 * self.B * self.Hq * self.Nq * self.Nk * self.d
+        return f / 2.0 if self.causal else f
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    workload: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    Nk_max: int
+    len_lo: int
+    len_hi: int
+    chunk: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+CONFIGS: Dict[str, object] = {
+    "c1": PrefillConfig("c1", "noncausal single-head fp32 B=1 H=1 N=128 d=64",
+                        B=1, Hq=1, Hkv=1, Nq=128, Nk=128, d=64, causal=False, dtype="f32"),
+    "c2": PrefillConfig("c2", "causal MHA prefill bf16 B=2 H=12 N=2048 d=64",
+                        B=2, Hq=12, Hkv=12, Nq=2048, Nk=2048, d=64, causal=True, dtype="bf16"),
+    "c3": PrefillConfig("c3", "causal MHA prefill bf16 B=1 H=32 N=8192 d=128 (Q,K x1.5)",
+                        B=1, Hq=32, Hkv=32, Nq=8192, Nk=8192, d=128, causal=True, dtype="bf16",
+                        qk_gain=1.5),
+    "c4": PrefillConfig("c4", "causal GQA prefill bf16 B=1 Hq=64 Hkv=8 N=32768 d=128",
+                        B=1, Hq=64, Hkv=8, Nq=32768, Nk=32768, d=128, causal=True, dtype="bf16"),
+    "c5": DecodeConfig("c5", "GQA split-KV decode bf16 B=16 Hq=64 Hkv=8 d=128 "
+                       "L~U[4096,32768] chunk=256",
+                       B=16, Hq=64, Hkv=8, d=128, Nk_max=32768, len_lo=4096, len_hi=32768,
+                       chunk=256),
+}
+
+
+def _round(x: torch.Tensor, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)
+    if dtype == "f32":
+        return x
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def prefill_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, dtype: str = "bf16",
+                   seed: int = 0, qk_gain: float = 1.0):
+    """Q [B,Nq,Hq,d], K and V [B,Nk,Hkv,d] on the CPU, drawn in the order Q, K, V."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((B, Nq, Hq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32)
+    if qk_gain != 1.0:
+        q.mul_(qk_gain)
+        k.mul_(qk_gain)
+    return _round(q, dtype), _round(k, dtype), _round(v, dtype)
+
+
+def prefill_inputs_for(cfg: PrefillConfig, seed: int = 0):
+    return prefill_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.dtype, seed,
+                          cfg.qk_gain)
+
+
+def decode_lengths(B: int, lo: int, hi: int, seed: int = 0,
+                   g: Optional[torch.Generator] = None) -> torch.Tensor:
+    """Per-sequence key counts, uniform on [lo, hi] inclusive (int32)."""
+    if g is None:
+        g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+def decode_inputs(B: int, Hq: int, Hkv: int, d: int, Nk_max: int, lo: int, hi: int,
+                  seed: int = 0, nan_pad: bool = True, lengths: Optional[torch.Tensor] = None):
+    """(lengths int32 [B], q bf16 [B,Hq,d], k_cache, v_cache bf16 [B,Nk_max,Hkv,d]).
+
+    Draw order: lengths (unless given), q, K cache, V cache.  Rows at or beyond
+    a sequence's length are NaN when ``nan_pad`` is set.
+    """
+    g = torch.Generator("cpu").manual_seed(seed)
+    if lengths is None:
+        lengths = decode_lengths(B, lo, hi, g=g)
+    else:
+        lengths = lengths.to(torch.int32).clone()
+    q = torch.randn((B, Hq, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    kc = torch.randn((B, Nk_max, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    vc = torch.randn((B, Nk_max, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    if nan_pad:
+        for b in range(B):
+            L = int(lengths[b])
+            kc[b, L:] = float("nan")
+            vc[b, L:] = float("nan")
+    return lengths, q, kc, vc
+
+
+def decode_inputs_for(cfg: DecodeConfig, seed: int = 0, nan_pad: bool = True):
+    return decode_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.Nk_max, cfg.len_lo, cfg.len_hi,
+                         seed, nan_pad)
+
+
+def decode_bytes(lengths, Hq: int, Hkv: int, d: int) -> float:
+    """Compulsory HBM bytes of one decode step: K and V of the valid keys (bf16),
+    plus q (bf16), O (fp32) and LSE (fp32), each counted once."""
+    total_keys = int(sum(int(x) for x in lengths))
+    B = len(lengths)
+    kv = 2.0 * total_keys * Hkv * d * 2
+    return kv + B * Hq * d * 2 + B * Hq * d * 4 + B * Hq * 4
