@@ -1,0 +1,235 @@
+"""Benchmark of the FlashAttention forward hot path on one MI355X.
+
+One step = one pass of the whole hot path on resident synthetic inputs:
+  * prefill: fa_forward on the causal GQA long-context workload
+    (bf16, B=1, Hq=64, Hkv=8, N=32768, d=128) — one kernel launch;
+  * decode:  fa_decode_splitkv on the GQA decode workload (bf16, B=16, Hq=64,
+    Hkv=8, d=128, per-sequence key counts ~U[4096, 32768], 256-key chunks) —
+    the split kernel and the merge kernel.
+`value` is the prefill's algorithmic TFLOP/s (4*B*Hq*Nq*Nk*d / 2 for causal) over
+its measured kernel time; the decode's HBM GB/s (compulsory K/V/q/O/LSE bytes)
+is reported alongside.  Kernel times come from HIP events recorded on the
+stream the kernels are launched on (torch's current stream), around every
+launch of the timed region.
+
+Prints ONE JSON line.  `python bench.py --gpus N` with N > 1 exits: this build
+runs on one GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill", default="c4", choices=["c2", "c3", "c4"],
+                    help="prefill workload (default: the long-context GQA one)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calib():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes_each_way": n, "launches": 3}))
+
+
+def cpu_baseline_prefill(cfg, target_s):
+    """The fp64 oracle on a bounded sample of the prefill workload: the last R query
+    rows of query head 0 (each sees ~all keys), R grown until ~target_s."""
+    import torch
+    import oracle
+    import workloads as W
+    q, k, v = W.prefill_inputs_for(cfg)
+    N, d = cfg.Nq, cfg.d
+    R = 64
+    t_used = 0.0
+    while True:
+        r0 = N - R
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, cfg.scale, cfg.causal, heads=[0], rows=(r0, N), row_block=256)
+        dt = time.perf_counter() - t0
+        if dt * 2 > target_s or R >= N:
+            break
+        t_used += dt
+        R = min(N, R * 2)
+    if cfg.causal:
+        keys = sum(min(cfg.Nk, i + (cfg.Nk - cfg.Nq) + 1) for i in range(r0, N))
+    else:
+        keys = R * cfg.Nk
+    flops = 4.0 * d * keys
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{cfg.name}: query head 0, query rows {r0}..{N - 1} ({R} rows, "
+                      f"{keys} visible (row,key) pairs), fp64 torch CPU standard attention"}
+
+
+def cpu_baseline_decode(cfg, lengths, q, kc, vc, target_s):
+    import torch
+    import oracle
+    import workloads as W
+    bs = []
+    t_total = 0.0
+    byts = 0.0
+    for b in range(cfg.B):
+        t0 = time.perf_counter()
+        oracle.decode_attention(q, kc, vc, lengths, cfg.scale, batches=[b])
+        t_total += time.perf_counter() - t0
+        bs.append(b)
+        byts += W.decode_bytes([int(lengths[b])], cfg.Hq, cfg.Hkv, cfg.d)
+        if t_total > target_s:
+            break
+    return {"value": byts / t_total / 1e9, "unit": "GB/s", "cores": torch.get_num_threads(),
+            "kind": "oracle", "seconds": round(t_total, 3),
+            "sample": f"{cfg.name}: sequences {bs} (all {cfg.Hq} query heads), fp64 torch CPU"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(no collectives or sharding are implemented).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calib:
+        copy_calib()
+        return
+    import io_aware_attention_attn_amd as fa
+    import workloads as W
+
+    dev = torch.device("cuda", 0)
+    pcfg = W.CONFIGS[args.prefill]
+    dcfg = W.CONFIGS["c5"]
+
+    print(f"[bench] generating {pcfg.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = W.prefill_inputs_for(pcfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty((pcfg.B, pcfg.Nq, pcfg.Hq, pcfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((pcfg.B, pcfg.Hq, pcfg.Nq), dtype=torch.float32, device=dev)
+
+    dec = None
+    if not args.no_decode:
+        print(f"[bench] generating {dcfg.name} inputs", file=sys.stderr, flush=True)
+        lengths, dq, kc, vc = W.decode_inputs_for(dcfg)
+        dec = dict(lengths=lengths, q=dq, kc=kc, vc=vc,
+                   dq=dq.to(dev), dkc=kc.to(dev), dvc=vc.to(dev), dl=lengths.to(dev))
+        dec["o"] = torch.empty((dcfg.B, dcfg.Hq, dcfg.d), dtype=torch.float32, device=dev)
+        dec["lse"] = torch.empty((dcfg.B, dcfg.Hq), dtype=torch.float32, device=dev)
+        nbytes = fa.fa_decode_splitkv_workspace_bytes(dcfg.B, dcfg.Hq, dcfg.Nk_max, dcfg.d,
+                                                      dcfg.chunk)
+        dec["ws"] = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        fa.fa_forward(qd, kd, vd, scale=pcfg.scale, causal=pcfg.causal, o=o, lse=lse)
+
+    def decode():
+        fa.fa_decode_splitkv(dec["dq"], dec["dkc"], dec["dvc"], dec["dl"], scale=dcfg.scale,
+                             chunk=dcfg.chunk, o=dec["o"], lse=dec["lse"], workspace=dec["ws"])
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        prefill()
+        if dec:
+            decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    print("[bench] timed region", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        prefill()
+        ev[i][1].record()
+        if dec:
+            ev[i][2].record()
+            decode()
+            ev[i][3].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    avg_pre = sum(pre_ms) / K
+    flops = pcfg.flops()
+    tflops = flops / (avg_pre * 1e-3) / 1e12
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
+
+    result = {
+        "metric": "attn fwd TFLOP/s and % bf16 MFMA peak (prefill); decode HBM GB/s and % peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs rounded to bf16; no dataset or weights)",
+        "config": {"workload": pcfg.workload, "B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv,
+                   "seq_len": pcfg.Nq, "head_dim": pcfg.d, "causal": pcfg.causal,
+                   "decode_workload": None if not dec else dcfg.workload,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, causal>",
+                     "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(avg_pre, 4),
+                     "flop_per_launch": flops},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if dec:
+        dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
+        avg_dec = sum(dec_ms) / K
+        dbytes = W.decode_bytes(dec["lengths"].tolist(), dcfg.Hq, dcfg.Hkv, dcfg.d)
+        gbs = dbytes / (avg_dec * 1e-3) / 1e9
+        result["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
+                            "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "avg_call_ms": round(avg_dec, 4),
+                            "kernels": "split + merge (one call)",
+                            "bytes_per_call": dbytes,
+                            "sum_seqlens": int(dec["lengths"].sum().item())}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_prefill(pcfg, args.cpu_seconds)
+        if dec:
+            result["decode"]["cpu_baseline"] = cpu_baseline_decode(
+                dcfg, dec["lengths"], dec["q"], dec["kc"], dec["vc"], args.cpu_seconds / 3)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

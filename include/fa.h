@@ -1,0 +1,149 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) FlashAttention forward library.
+ *
+ * The library computes exact attention O = softmax(scale * Q K^T) V tile by
+ * tile, with the online-softmax update, never writing the score matrix S or
+ * the probability matrix P to device memory.  Sources (cited by section):
+ *
+ *   [FA-notes]   "flash-attn" notes, minjae-portfolio.vercel.app/notes/flash-attn
+ *                §3 tiling and fusion, §4 online softmax, §5.2 forward kernel sketch
+ *                (per Q tile: loop over K/V tiles, keep row max m and row sum l,
+ *                rescale the output accumulator, store the statistics).
+ *   [FA-evo]     "Attention is All You Need부터 FlashAttention-3까지: Transformer
+ *                Attention 메커니즘의 진화와 O(1) 메모리 최적화 실전 구현", tildalice.io,
+ *                section "실전 구현": [batch, seq, heads, head_dim] tensors, causal
+ *                masking, bf16/fp16 inputs.
+ *   [LLM-basics] "LLM 기초 — Attention부터 FlashAttention까지", gylee815.github.io/llmso/w1,
+ *                ①-2 scaled dot-product attention, ①-7 causal mask, ②-3/②-4 KV cache
+ *                and decode, ②-7 GQA, ③-1 safe softmax, ③-2 online softmax,
+ *                ③-5 FlashAttention's tile loop.
+ *   [FA3-entry]  "FlashAttention-3 (FA-3)", itpe.jackerlab.com, §2 (MQA/GQA support)
+ *                and §4 (FlashDecoding, an inference-time attention kernel).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, contiguous, row-major, 16-byte
+ *     aligned.  The caller owns every buffer; the library allocates nothing,
+ *     keeps no state and never synchronises.  Work is enqueued on `stream`
+ *     (NULL = the default stream) and the call returns right after the launch.
+ *   - Arguments are validated on the host before any HIP call; a negative
+ *     fa_status is returned and nothing is launched.  A launch failure reported
+ *     by hipGetLastError returns FA_ERR_HIP.  Device-side faults surface at the
+ *     caller's next synchronisation.
+ *   - Layouts: Q and O are [B, Nq, Hq, d]; K and V are [B, Nk, Hkv, d]; the
+ *     log-sum-exp LSE is [B, Hq, Nq] in natural-log units of the scaled score,
+ *     LSE_i = m_i + ln l_i with m_i = max_j S_ij and l_i = sum_j exp(S_ij - m_i).
+ *     (The [FA-notes] §5.2 sketch stores l and m separately; LSE carries the same
+ *     information: P_ij = exp(S_ij - LSE_i).)
+ *   - GQA ([LLM-basics] ②-7): Hq must be a multiple of Hkv; query head h reads
+ *     K/V head h / (Hq / Hkv) (consecutive query heads share a K/V head).
+ *   - Causal ([LLM-basics] ①-7): key j is visible from query row i iff
+ *     j <= i + (Nk - Nq) (rows aligned to the end of the key sequence; for
+ *     Nq == Nk this is "token i sees tokens 0..i").  causal with Nq > Nk is
+ *     rejected because some rows would see no key at all.
+ *   - d (head dimension) must be 64 or 128.
+ *   - Thread safety: every function may be called concurrently from several
+ *     host threads; calls on one stream execute in stream order.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,       /* B, H, N or d <= 0; Hq % Hkv != 0; causal with Nq > Nk;
+                              sizes whose element counts overflow 32-bit row indexing */
+  FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}; decode chunk not a positive multiple of 64 */
+  FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = -5,   /* decode workspace missing or smaller than required */
+  FA_ERR_HIP = -6          /* the kernel launch failed (hipGetLastError) */
+} fa_status;
+
+/*
+ * fa_forward — prefill / full-sequence forward, bf16 inputs.
+ *
+ * [FA-notes] §3-§5.2, [LLM-basics] ③-5: for every (batch, query head, block of
+ * query rows) the kernel keeps the Q block on chip, streams the K/V blocks of
+ * the matching K/V head through on-chip memory, and for each block updates the
+ * running row max m, the running row sum l and the output accumulator
+ * (m_new = max(m, block max); acc and l rescaled by exp(m - m_new)).  At the
+ * end O = acc / l and LSE = m + ln l are written.  Causal runs skip key blocks
+ * that lie wholly in the future of a query block and mask only the blocks that
+ * cross the diagonal.
+ *
+ *   q      bf16  [B, Nq, Hq, d]   (read)
+ *   k, v   bf16  [B, Nk, Hkv, d]  (read)
+ *   o      fp32  [B, Nq, Hq, d]   (written; every element)
+ *   lse    fp32  [B, Hq, Nq]      (written; every element)
+ *   scale  multiplier of Q K^T (1/sqrt(d) for standard attention)
+ *   causal 0 or 1
+ * Scores and the softmax are computed in fp32; QK^T and P V are bf16 x bf16
+ * products accumulated in fp32 (P is rounded to bf16 for the second product).
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+               hipStream_t stream);
+
+/*
+ * fa_forward_f32 — the same contract with fp32 Q, K, V.  Everything, including
+ * the probabilities multiplied into V, stays in fp32 (nothing is rounded to a
+ * 16-bit type).
+ */
+int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   hipStream_t stream);
+
+/*
+ * fa_decode_splitkv_workspace_bytes — bytes of device workspace that
+ * fa_decode_splitkv needs for these sizes (per-chunk partial outputs and
+ * log-sum-exps in fp32).  Returns 0 for invalid sizes.
+ */
+size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int chunk);
+
+/*
+ * fa_decode_splitkv — one decode step over a padded KV cache, split over keys.
+ *
+ * [LLM-basics] ②-3/②-4: a single new query token per sequence attends to all
+ * of that sequence's cached keys and values; [FA3-entry] §4 names a dedicated
+ * decode kernel.  The keys of sequence b are cut into chunks of `chunk` keys;
+ * kernel 1 computes, for every (b, K/V head, chunk), the attention of all
+ * Hq/Hkv query heads of that group to the chunk's keys: the chunk-normalised
+ * output O_c and lse_c.  Kernel 2 merges the chunks of each (b, query head)
+ * with the two-block online-softmax merge of [FA-notes] §4 applied across all
+ * chunks: LSE = M + ln sum_c exp(lse_c - M), O = sum_c exp(lse_c - LSE) O_c.
+ *
+ *   q          bf16  [B, Hq, d]             (read)
+ *   k_cache    bf16  [B, Nk_max, Hkv, d]    (read; rows >= seqlens_k[b] are never read)
+ *   v_cache    bf16  [B, Nk_max, Hkv, d]    (read; rows >= seqlens_k[b] are never read)
+ *   seqlens_k  int32 [B] on the device; 1 <= seqlens_k[b] <= Nk_max is the caller's
+ *              contract.  The kernels clamp it to [0, Nk_max] for memory safety;
+ *              a sequence with 0 keys gets O = 0 and LSE = -inf.
+ *   o          fp32  [B, Hq, d]             (written)
+ *   lse        fp32  [B, Hq]                (written)
+ *   chunk      keys per split, a positive multiple of 64 (256 for the standard setup)
+ *   workspace  device buffer of at least fa_decode_splitkv_workspace_bytes(...)
+ *              bytes, 16-byte aligned, owned by the caller; its contents on entry
+ *              do not matter and are overwritten.
+ * The two kernels run in order on `stream`; stream order is the only
+ * synchronisation between them.  Returns FA_OK or a negative fa_status.
+ */
+int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seqlens_k, float* o, float* lse,
+                      int B, int Hq, int Hkv, int Nk_max, int d, float scale, int chunk,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* fa_status_str — a static, human-readable string for a status code. */
+const char* fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

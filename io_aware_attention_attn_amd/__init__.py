@@ -1,0 +1,169 @@
+"""Python binding of libfa.so, the MI355X (gfx950) FlashAttention forward library.
+
+The C ABI is declared in ``include/fa.h``.  This module only marshals arguments:
+it checks what it needs to read sizes off torch tensors, allocates outputs and
+workspace with torch (device memory plumbing), passes raw device pointers and the
+current HIP stream, and turns a negative status into ``ValueError``.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback path.
+
+Functions (same names as the C entry points):
+  fa_forward(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None)
+  fa_forward_f32(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None)
+  fa_decode_splitkv_workspace_bytes(B, Hq, Nk_max, d, chunk=256)
+  fa_decode_splitkv(q, k_cache, v_cache, seqlens_k, scale=None, chunk=256, o=None,
+                    lse=None, workspace=None, stream=None)
+  fa_status_str(status)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_UNSUPPORTED = -3
+FA_ERR_ALIGN = -4
+FA_ERR_WORKSPACE = -5
+FA_ERR_HIP = -6
+
+_lib = None
+
+
+class FAError(ValueError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_str(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (raises if it has not been built; there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m io_aware_attention_attn_amd._build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.fa_forward.restype = i
+    L.fa_forward_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.fa_forward_f32.restype = i
+    L.fa_decode_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.fa_decode_splitkv_workspace_bytes.restype = sz
+    L.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    L.fa_decode_splitkv.restype = i
+    L.fa_status_str.argtypes = [i]
+    L.fa_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def fa_status_str(status: int) -> str:
+    return lib().fa_status_str(int(status)).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_tensor(t, name, dtype, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _forward(entry, q, k, v, scale, causal, o, lse, stream, dtype) -> Tuple:
+    import torch
+    _check_tensor(q, "q", dtype, 4)
+    _check_tensor(k, "k", dtype, 4)
+    _check_tensor(v, "v", dtype, 4)
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Nq, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_tensor(o, "o", torch.float32, 4)
+    _check_tensor(lse, "lse", torch.float32, 3)
+    if tuple(o.shape) != (B, Nq, Hq, d) or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("o / lse have the wrong shape")
+    st = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+               float(scale), 1 if causal else 0, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, entry.__name__)
+    return o, lse
+
+
+def fa_forward(q, k, v, scale: Optional[float] = None, causal: bool = False, o=None, lse=None,
+               stream=None):
+    """bf16 q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d] -> (O fp32 [B,Nq,Hq,d], LSE fp32 [B,Hq,Nq])."""
+    import torch
+    return _forward(lib().fa_forward, q, k, v, scale, causal, o, lse, stream, torch.bfloat16)
+
+
+def fa_forward_f32(q, k, v, scale: Optional[float] = None, causal: bool = False, o=None,
+                   lse=None, stream=None):
+    """fp32 variant of fa_forward (no 16-bit rounding anywhere)."""
+    import torch
+    return _forward(lib().fa_forward_f32, q, k, v, scale, causal, o, lse, stream, torch.float32)
+
+
+def fa_decode_splitkv_workspace_bytes(B: int, Hq: int, Nk_max: int, d: int, chunk: int = 256) -> int:
+    return int(lib().fa_decode_splitkv_workspace_bytes(B, Hq, Nk_max, d, chunk))
+
+
+def fa_decode_splitkv(q, k_cache, v_cache, seqlens_k, scale: Optional[float] = None,
+                      chunk: int = 256, o=None, lse=None, workspace=None, stream=None):
+    """q bf16 [B,Hq,d]; caches bf16 [B,Nk_max,Hkv,d]; seqlens_k int32 [B] on the GPU
+    -> (O fp32 [B,Hq,d], LSE fp32 [B,Hq])."""
+    import torch
+    _check_tensor(q, "q", torch.bfloat16, 3)
+    _check_tensor(k_cache, "k_cache", torch.bfloat16, 4)
+    _check_tensor(v_cache, "v_cache", torch.bfloat16, 4)
+    _check_tensor(seqlens_k, "seqlens_k", torch.int32, 1)
+    B, Hq, d = q.shape
+    Bc, Nk_max, Hkv, dc = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or Bc != B or dc != d or seqlens_k.shape[0] != B:
+        raise ValueError("decode shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = fa_decode_splitkv_workspace_bytes(B, Hq, Nk_max, d, chunk)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o),
+                                 _ptr(lse), B, Hq, Hkv, Nk_max, d, float(scale), int(chunk),
+                                 _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                 _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_splitkv")
+    return o, lse

@@ -1,0 +1,110 @@
+// fa_api.hip — the C ABI declared in include/fa.h: host-side validation, kernel
+// selection and launch.  Validation happens before any HIP call; nothing here
+// allocates, synchronises or keeps state.
+#include "fa.h"
+
+#include <limits.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Shared checks for the two prefill entry points.
+int check_prefill(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // Row indices and the 1-D grid are 32-bit: keep B*N*H and the block count in range.
+  if ((long long)B * Nq * Hq > INT_MAX || (long long)B * Nk * Hkv > INT_MAX) return FA_ERR_SHAPE;
+  if ((long long)B * Hq * ((Nq + 15) / 16) > INT_MAX) return FA_ERR_SHAPE;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int max_chunks_of(int Nk_max, int chunk) { return (Nk_max + chunk - 1) / chunk; }
+
+int check_decode_sizes(int B, int Hq, int Hkv, int Nk_max, int d, int chunk) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nk_max <= 0 || d <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if ((long long)B * Nk_max * Hkv > INT_MAX) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (chunk <= 0 || chunk % 64 != 0) return FA_ERR_UNSUPPORTED;
+  const long long mc = max_chunks_of(Nk_max, chunk);
+  const long long G = Hq / Hkv;
+  if (mc > 0x7fffffffLL || (long long)Hkv * ((G + 15) / 16) > 65535 || B > 65535)
+    return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
+               int Hkv, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream) {
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal);
+  if (st != FA_OK) return st;
+  fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal ? 1 : 0};
+  return fa::launch_prefill_bf16(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   hipStream_t stream) {
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal);
+  if (st != FA_OK) return st;
+  fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal ? 1 : 0};
+  return fa::launch_prefill_f32(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int chunk) {
+  if (check_decode_sizes(B, Hq, 1, Nk_max, d, chunk) != FA_OK) return 0;
+  const int mc = max_chunks_of(Nk_max, chunk);
+  return fa::decode_part_o_bytes(B, Hq, mc, d) + fa::decode_part_lse_bytes(B, Hq, mc);
+}
+
+int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seqlens_k, float* o, float* lse, int B, int Hq, int Hkv,
+                      int Nk_max, int d, float scale, int chunk, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !seqlens_k || !o || !lse) return FA_ERR_NULL;
+  const int st = check_decode_sizes(B, Hq, Hkv, Nk_max, d, chunk);
+  if (st != FA_OK) return st;
+  if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(o) ||
+      (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return FA_ERR_ALIGN;
+  const int mc = max_chunks_of(Nk_max, chunk);
+  const size_t need = fa::decode_part_o_bytes(B, Hq, mc, d) + fa::decode_part_lse_bytes(B, Hq, mc);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return FA_ERR_ALIGN;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             fa::decode_part_o_bytes(B, Hq, mc, d));
+  fa::DecodeArgs a{q, k_cache, v_cache, seqlens_k, o, lse, part_o, part_lse,
+                   B, Hq, Hkv, Nk_max, d, chunk, mc, scale};
+  return fa::launch_decode_splitkv(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (non-positive, Hq % Hkv != 0, causal "
+                              "with Nq > Nk, or too large for 32-bit indexing)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128; decode chunk "
+                                    "must be a positive multiple of 64";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: decode workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+    default: return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

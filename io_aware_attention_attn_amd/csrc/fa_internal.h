@@ -1,0 +1,53 @@
+// fa_internal.h — argument blocks and launchers shared between the C ABI (fa_api.hip)
+// and the kernel translation units.  Not part of the public interface (include/fa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Prefill forward: Q [B,Nq,Hq,d], K/V [B,Nk,Hkv,d], O [B,Nq,Hq,d] fp32, LSE [B,Hq,Nq] fp32.
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+};
+
+// Split-KV decode: q [B,Hq,d], caches [B,Nk_max,Hkv,d], seqlens [B] (device),
+// O [B,Hq,d] fp32, LSE [B,Hq] fp32, workspace = partial O [B,Hq,C,d] fp32 followed by
+// partial LSE [B,Hq,C] fp32 with C = ceil(Nk_max / chunk).
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* seqlens;
+  float* o;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int B, Hq, Hkv, Nk_max, d, chunk, max_chunks;
+  float scale;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t s);
+
+// Workspace split used by both the size query and the launcher.
+inline size_t decode_part_o_bytes(int B, int Hq, int max_chunks, int d) {
+  size_t n = (size_t)B * Hq * max_chunks * d * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+inline size_t decode_part_lse_bytes(int B, int Hq, int max_chunks) {
+  size_t n = (size_t)B * Hq * max_chunks * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+}  // namespace fa

@@ -89,7 +89,8 @@ def attention(q, k, v, scale: float, causal: bool, row_block: Optional[int] = No
     range [r0, r1); entries outside are left as NaN.  ``row_block`` bounds the
     memory of S and P by processing that many query rows at a time.
     """
-    q, k, v = _as64(q), _as64(k), _as64(v)
+    if not isinstance(q, torch.Tensor):
+        q, k, v = _as64(q), _as64(k), _as64(v)
     B, Nq, Hq, d = q.shape
     _, Nk, Hkv, _ = k.shape
     group = Hq // Hkv
@@ -100,11 +101,11 @@ def attention(q, k, v, scale: float, causal: bool, row_block: Optional[int] = No
     for b in range(B):
         for h in (heads if heads is not None else range(Hq)):
             kvh = h // group
-            kk = k[b, :, kvh, :]
-            vv = v[b, :, kvh, :]
+            kk = _as64(k[b, :, kvh, :])   # fp64 copies of just the slices in use
+            vv = _as64(v[b, :, kvh, :])
             for a in range(r0, r1, step):
                 e_ = min(a + step, r1)
-                s = _scores(q[b, a:e_, h, :], kk, scale, a, Nq, causal)
+                s = _scores(_as64(q[b, a:e_, h, :]), kk, scale, a, Nq, causal)
                 m = torch.amax(s, dim=1, keepdim=True)
                 ex = torch.exp(s - m)
                 l = torch.sum(ex, dim=1, keepdim=True)

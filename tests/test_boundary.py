@@ -1,0 +1,143 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/fa.h declares,
+and rejects invalid arguments with the documented status before any HIP call.
+
+Only calls that fail validation are made here (no device is needed for those);
+nothing is launched.  Pointer arguments are fake, aligned, non-null addresses:
+validation returns before they could ever be dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_attention_attn_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+P = 0x10000          # fake, 16-byte aligned, never dereferenced
+MIS = 0x10004        # 4-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.skip("libfa.so not built (run python -m io_aware_attention_attn_amd._build)")
+    return fa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == {"fa_forward", "fa_forward_f32", "fa_decode_splitkv_workspace_bytes",
+                          "fa_decode_splitkv", "fa_status_str"}
+    for n in names:
+        assert hasattr(L, n), f"libfa.so does not export {n}"
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        s = fa.fa_status_str(st)
+        assert s.startswith("FA_"), s
+    assert "unknown" in fa.fa_status_str(-99)
+
+
+def _fwd(L, entry, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.125,
+         causal=0):
+    return getattr(L, entry)(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("entry", ["fa_forward", "fa_forward_f32"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(k=None), fa.FA_ERR_NULL),
+    (dict(v=None), fa.FA_ERR_NULL),
+    (dict(o=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(Hq=-1), fa.FA_ERR_SHAPE),
+    (dict(Hkv=0), fa.FA_ERR_SHAPE),
+    (dict(Nq=0), fa.FA_ERR_SHAPE),
+    (dict(Nk=0), fa.FA_ERR_SHAPE),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_SHAPE),
+    (dict(Nq=9, Nk=8, causal=1), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=MIS), fa.FA_ERR_ALIGN),
+    (dict(v=MIS), fa.FA_ERR_ALIGN),
+    (dict(o=MIS), fa.FA_ERR_ALIGN),
+    (dict(B=1 << 20, Nq=1 << 12, Hq=1 << 10, Hkv=1 << 10, Nk=8), fa.FA_ERR_SHAPE),
+])
+def test_forward_rejects(L, entry, kw, status):
+    assert _fwd(L, entry, **kw) == status
+
+
+def test_workspace_bytes(L):
+    n = fa.fa_decode_splitkv_workspace_bytes(16, 64, 32768, 128, 256)
+    chunks = 32768 // 256
+    want_o = 16 * 64 * chunks * 128 * 4
+    want_l = 16 * 64 * chunks * 4
+    assert n == ((want_o + 255) // 256) * 256 + ((want_l + 255) // 256) * 256
+    assert fa.fa_decode_splitkv_workspace_bytes(1, 1, 1, 64, 64) > 0
+    for bad in [(0, 1, 1, 64, 256), (1, 1, 0, 64, 256), (1, 1, 1, 80, 256), (1, 1, 1, 64, 100),
+                (1, 1, 1, 64, 0)]:
+        assert fa.fa_decode_splitkv_workspace_bytes(*bad) == 0, bad
+
+
+def _dec(L, q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nk_max=512, d=128, scale=0.1,
+         chunk=256, ws=P, ws_bytes=1 << 30):
+    return L.fa_decode_splitkv(q, kc, vc, sl, o, lse, B, Hq, Hkv, Nk_max, d, scale, chunk, ws,
+                               ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(kc=None), fa.FA_ERR_NULL),
+    (dict(sl=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
+    (dict(Nk_max=0), fa.FA_ERR_SHAPE),
+    (dict(d=100), fa.FA_ERR_UNSUPPORTED),
+    (dict(chunk=100), fa.FA_ERR_UNSUPPORTED),
+    (dict(chunk=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=MIS), fa.FA_ERR_ALIGN),
+    (dict(kc=MIS), fa.FA_ERR_ALIGN),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
+    (dict(ws=MIS), fa.FA_ERR_ALIGN),
+])
+def test_decode_rejects(L, kw, status):
+    assert _dec(L, **kw) == status
+
+
+def test_binding_raises_without_gpu_tensors(L):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((1, 4, 1, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_forward(q, q, q)
+    with pytest.raises(TypeError):
+        fa.fa_forward(q.float(), q, q)
+
+
+def test_product_does_not_import_oracle():
+    """The product package and the oracle share no code: no import either way."""
+    pkg = os.path.join(ROOT, "io_aware_attention_attn_amd")
+    imp_oracle = re.compile(r"^\s*(from\s+oracle\b|import\s+oracle\b)|#include\s+\"[^\"]*oracle", re.M)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not imp_oracle.search(src), f
+    imp_pkg = re.compile(r"^\s*(from|import)\s+io_aware_attention_attn_amd\b", re.M)
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith(".py"):
+            src = open(os.path.join(ROOT, "oracle", f)).read()
+            assert not imp_pkg.search(src), f
