@@ -23,6 +23,9 @@ int check_prefill(const void* q, const void* k, const void* v, const float* o, c
   // Row indices and the 1-D grid are 32-bit: keep B*N*H and the block count in range.
   if ((long long)B * Nq * Hq > INT_MAX || (long long)B * Nk * Hkv > INT_MAX) return FA_ERR_SHAPE;
   if ((long long)B * Hq * ((Nq + 15) / 16) > INT_MAX) return FA_ERR_SHAPE;
+  // Buffer addressing inside one batch's slice uses 32-bit byte offsets.
+  if ((long long)(Nq + 256) * Hq * d * 4 > INT_MAX || (long long)(Nk + 256) * Hkv * d * 4 > INT_MAX)
+    return FA_ERR_SHAPE;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
     return FA_ERR_ALIGN;
   return FA_OK;

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     float* __restrict__ part_lse, int Hq, int Hkv, int Nk_max, int chunk, int max_chunks,
     int n_qgroups, float c) {
   constexpr int VT_BYTES = kWaves * D * (kSub + kVPad) * 2;
-  constexpr int MERGE_BYTES = kWaves * 16 * (D + 4) * 4 + 2 * kWaves * 16 * 4;
+  constexpr int MERGE_BYTES = kWaves * 16 * (D + 4) * 4 + 3 * kWaves * 16 * 4;
   constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
 
@@ -97,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   f32x4 acc[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{};
-  float m_run = kNegInf, l_run = 0.f;
+  // l_run sums the bf16-rounded weights (O's normaliser), l_lse the unrounded ones.
+  float m_run = kNegInf, l_run = 0.f, l_lse = 0.f;
 
   // V loading: a lane owns column chunk vcc (8 d) of 4-key runs kq, kq+KQ, ...
   constexpr int CPR = D / 8;          // 16-byte chunks per key row
@@ -171,28 +172,33 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
-    float rs = 0.f;
+    float ex = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(s[kb][r] - m_use);
-        s[kb][r] = p;
-        rs += p;
+        s[kb][r] = fast_exp2(s[kb][r] - m_use);
+        ex += s[kb][r];
       }
-    l_run = l_run * alpha + rs;
+    l_lse = l_lse * alpha + ex;
     m_run = m_new;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
 
+    // P rounded to bf16 for the second product; the row sum adds those same rounded
+    // weights, so the chunk output is a true weighted mean of V.
     bf16x8 pf[2];
+    float rs = 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       u32x4 w = {pack_bf16x2(s[2 * u][0], s[2 * u][1]), pack_bf16x2(s[2 * u][2], s[2 * u][3]),
                  pack_bf16x2(s[2 * u + 1][0], s[2 * u + 1][1]),
                  pack_bf16x2(s[2 * u + 1][2], s[2 * u + 1][3])};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) rs = sum_bf16x2(w[t], rs);
       pf[u] = __builtin_bit_cast(bf16x8, w);
     }
+    l_run = l_run * alpha + rs;
     // The wave's own LDS writes must land before its lanes read each other's data.
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
@@ -210,18 +216,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   // Row sums across the four lane groups that share a query.
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  l_lse += __shfl_xor(l_lse, 16);
+  l_lse += __shfl_xor(l_lse, 32);
 
   // Merge the four waves through LDS (the V slices are dead by now).
   __syncthreads();
   float* mo = reinterpret_cast<float*>(smem);                 // [4][16][D+4]
   float* mm = mo + kWaves * 16 * (D + 4);                     // [4][16]
   float* ml = mm + kWaves * 16;                               // [4][16]
+  float* mle = ml + kWaves * 16;                              // [4][16]
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
     *reinterpret_cast<f32x4*>(&mo[(wave * 16 + l16) * (D + 4) + db * 16 + 4 * grp]) = acc[db];
   if (grp == 0) {
     mm[wave * 16 + l16] = m_run;
     ml[wave * 16 + l16] = l_run;
+    mle[wave * 16 + l16] = l_lse;
   }
   __syncthreads();
 
@@ -234,11 +244,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * 16 + qi]);
     float wsc[kWaves];
-    float Lsum = 0.f;
+    float Lsum = 0.f, Lex = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       wsc[w] = fast_exp2(mm[w * 16 + qi] - M);  // 0 for a wave that saw no key
       Lsum += wsc[w] * ml[w * 16 + qi];
+      Lex += wsc[w] * mle[w * 16 + qi];
     }
     const float inv = 1.f / Lsum;
     const int hq = hq0 + qi;
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       *reinterpret_cast<f32x4*>(dst + i) = o * inv;
     }
     if (d0 == 0)
-      part_lse[((size_t)b * Hq + hq) * max_chunks + chunk_id] = (M + fast_log2(Lsum)) * kLn2;
+      part_lse[((size_t)b * Hq + hq) * max_chunks + chunk_id] = (M + fast_log2(Lex)) * kLn2;
   }
 }
 

@@ -36,6 +36,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+}
+
 __device__ __forceinline__ u32x4 ldg128(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -6,67 +6,117 @@
 // one workgroup owns a block of query rows of one (batch, query head).  It keeps
 // that Q block in registers and streams the K/V blocks of the matching K/V head
 // through LDS.  For each K/V block it forms the scores, updates the running row
-// maximum m and row sum l with the two-block merge (m_new = max(m_old, m_blk);
-// old sums and the output accumulator scaled by exp(m_old - m_new)), and adds
-// P V to the accumulator.  S and P live only in registers.  At the end
-// O = acc / l and LSE = m + ln l are written.
+// maximum and row sum with the two-block merge, rescales the output accumulator,
+// and adds P V to it.  S and P live only in registers.  At the end O = acc / l
+// and LSE = m + ln l are written.
 //
 // gfx950 mapping
-//   * 256 threads = 4 wave64s; each wave owns 32 query rows, the workgroup 128.
+//   * WAVES wave64s per workgroup, 32 query rows each.
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//     A = 32 keys x 16 d from LDS, B = Q^T fragment held in VGPRs for the whole
-//     loop.  In the 32x32 result every lane holds 16 keys of ONE query row
-//     (row = lane % 32), so a row maximum is an in-lane max over 32 values plus
-//     a single exchange between the two wave halves (v_permlane32_swap).
-//   * O^T = V^T P^T with the same instruction: A = V^T from LDS, B = P^T taken
-//     straight from the score registers (rounded to bf16).  The output lanes
-//     again hold one query row each, so the rescale by exp2(m_old - m_new) is a
-//     per-lane multiply.  The keys of the P fragment come in the order the score
-//     layout produces them; the transposed V tile in LDS is stored in that same
-//     permuted key order, so the contraction pairs the right key with the right
-//     value.
-//   * Scores are taken to base 2 with scale*log2(e) folded into one multiply,
-//     so every exponential is one v_exp_f32.
-//   * K/V blocks of 64 keys: the next block is fetched from HBM into registers
-//     while the current one is multiplied; K is stored row-major with a 16-byte
-//     row pad (conflict-free 128-bit reads), V is transposed in registers and
-//     stored [d][key].
+//     A = 32 keys x 16 d read from LDS, B = the Q^T fragment kept in VGPRs for the
+//     whole loop.  In the 32x32 result a lane holds 16 keys of ONE query row
+//     (row = lane % 32), so a row maximum is an in-lane max plus one exchange
+//     between the wave halves (v_permlane32_swap).
+//   * O^T = V^T P^T with the same instruction: B = P^T straight from the score
+//     registers (rounded to bf16), A = V^T read from the row-major V block with
+//     ds_read_b64_tr_b16 (the LDS unit transposes 4x4 blocks of 16-bit values in
+//     flight).  The keys of the P fragment come in the order the score layout
+//     produces them, and the transposed reads fetch V rows in that same order.
+//   * K/V blocks of 64 keys go from HBM straight into LDS (buffer_load ... lds, no
+//     VGPR staging), double-buffered.  K block j+2 and V block j+1 are in flight
+//     while block j is processed, so each iteration needs one barrier.
+//   * The scores of block j+1 (MFMA) are issued before the softmax of block j
+//     (VALU) so the two can overlap.
+//   * Row chunks in LDS are XOR-swizzled so the MFMA operand reads are free of
+//     bank conflicts.
+//   * exp2 with scale*log2(e) folded into one FMA per score.  The running maximum
+//     used for the exponent is only moved when a block's maximum exceeds it by
+//     more than kTau (base-2 units): the online-softmax identity holds for any
+//     common reference value, and a bounded lag keeps exp2 <= 2^kTau, so most
+//     blocks skip the accumulator rescale entirely.
+//   * Buffer loads clip at the end of each (batch, head) slice, so rows past Nq
+//     or Nk read as zeros without branches.
+//   * Workgroups are numbered so that each XCD (own L2) receives a contiguous slice
+//     of the work list, ordered (batch, K/V head) major, query block from the
+//     last (most keys under a causal mask) to the first, query heads of the GQA
+//     group minor: workgroups sharing K/V run together on one XCD.
 //   * Causal: key blocks wholly in the future of the workgroup's rows are never
-//     visited; only blocks that cross the diagonal (or the ragged end of the key
-//     sequence) are masked.  Workgroups are issued heaviest-first.
+//     visited; only blocks crossing the diagonal or the ragged end are masked.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per K/V block
-constexpr int kThreads = 256;  // four wave64s
-constexpr int kPad = 8;        // bf16 elements of padding per LDS row (16 bytes)
+constexpr float kTau = 8.f;    // largest lag of the exponent reference (base 2)
+constexpr int kNumXcd = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 
-template <int D>
-struct Smem {
-  uint16_t k[kBN][D + kPad];   // K block, [key][d]
-  uint16_t vt[D][kBN + kPad];  // V block transposed, [d][permuted key]
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-// Position of key `kk` (a multiple of 4 inside the block) in a transposed V row.
-// Within each 16-key group the four 4-key runs are stored in the order 0, 2, 1, 3,
-// which is the order in which the score layout hands keys to the P fragment
-// (wave half 0 supplies keys 0-3 and 8-11, half 1 supplies 4-7 and 12-15).
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int sub = (kk & 15) >> 2;
-  return (kk & ~15) + (sub & 1) * 8 + (sub >> 1) * 4;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int B,
-    int Hq, int Hkv, int Nq, int Nk, float c, int n_mblocks) {
+// XOR swizzles of the 16-byte chunk index inside an LDS row of D bf16.
+template <int D>
+struct Swz {
+  // K: 16 consecutive rows read at the same chunk land in 16 different bank groups.
+  static __device__ __forceinline__ int k(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  }
+  // V: the 4 rows x 4 chunks a half-wave touches in one transposed read are distinct.
+  static __device__ __forceinline__ int v(int row) {
+    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+  }
+};
+
+// Issue the loads of one 64-key block (rows n0.., all D columns) straight into LDS.
+// Each instruction fills 1 KB of LDS in lane order; the global chunk a lane fetches
+// is chosen so the LDS copy ends up swizzled.
+template <int D, int WAVES, bool IS_V>
+__device__ __forceinline__ void issue_block(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, int n0,
+                                            uint16_t* tile, int wave, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int INSTS = kBN * CH / 64;
+  constexpr int PER_WAVE = INSTS / WAVES;
+  static_assert(PER_WAVE * WAVES == INSTS, "block split");
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int inst = wave * PER_WAVE + i;
+    const int lin = inst * 64 + lane;
+    const int row = lin / CH;
+    const int pos = lin % CH;
+    const int c = pos ^ (IS_V ? Swz<D>::v(row) : Swz<D>::k(row));
+    const uint32_t voff = (uint32_t)(n0 + row) * row_bytes + (uint32_t)c * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + inst * 512), 16, voff, 0, 0,
+                                             0);
+  }
+}
+
+__device__ __forceinline__ int xcd_remap(int g, int T) {
+  const int q = T / kNumXcd, r = T % kNumXcd;
+  const int x = g % kNumXcd, i = g / kNumXcd;
+  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+template <int D, int WAVES, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64),
+                          amdgpu_waves_per_eu(2, 2))) void
+prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                    const uint16_t* __restrict__ V, float* __restrict__ O,
+                    float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk, float c,
+                    int n_mblocks) {
   static_assert(D == 64 || D == 128, "head dim");
-  __shared__ Smem<D> sm;
+  constexpr int BM = 32 * WAVES;
+  constexpr int NT = WAVES * 64;
+  __shared__ __attribute__((aligned(1024))) uint16_t ks[2][kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs[2][kBN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -74,196 +124,202 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Workgroup -> (query block, head, batch).  Query blocks are issued from the last
-  // (the most keys under a causal mask) to the first.
-  const int bh_count = B * Hq;
-  const int bid = blockIdx.x;
-  const int mb = n_mblocks - 1 - bid / bh_count;
-  const int bh = bid % bh_count;
-  const int hq = bh % Hq;
-  const int b = bh / Hq;
-  const int kvh = hq / (Hq / Hkv);
-  const int m0 = mb * kBM;
+  // ---- which work item: XCD slice, (batch, K/V head) major, heavy query blocks first
+  const int G = Hq / Hkv;
+  const int T = n_mblocks * B * Hq;
+  const int lam = xcd_remap((int)blockIdx.x, T);
+  const int hg = lam % G;
+  const int rest = lam / G;
+  const int mb = n_mblocks - 1 - rest % n_mblocks;
+  const int bk = rest / n_mblocks;
+  const int kvh = bk % Hkv;
+  const int b = bk / Hkv;
+  const int hq = kvh * G + hg;
+  const int m0 = mb * BM;
 
-  const size_t q_stride = (size_t)Hq * D;
-  const size_t kv_stride = (size_t)Hkv * D;
-  const uint16_t* Qb = Q + ((size_t)b * Nq * Hq + hq) * D;
-  const uint16_t* Kb = K + ((size_t)b * Nk * Hkv + kvh) * D;
-  const uint16_t* Vb = V + ((size_t)b * Nk * Hkv + kvh) * D;
+  const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
+  const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + ((size_t)b * Nq * Hq + hq) * D,
+                                              (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + ((size_t)b * Nk * Hkv + kvh) * D,
+                                              (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + ((size_t)b * Nk * Hkv + kvh) * D,
+                                              (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
 
-  // Q^T fragments: lane holds query row qrow, d = 16*s + 8*hi .. +7.
+  // ---- Q^T fragments: lane holds query row qrow, d = 16*s + 8*hi .. +7 (zeros past Nq)
   const int qrow = m0 + wave * 32 + l32;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (qrow < Nq) w = ldg128(Qb + (size_t)qrow * q_stride + 16 * s + 8 * hi);
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+        rq, (uint32_t)qrow * q_row_bytes + (uint32_t)(16 * s + 8 * hi) * 2, 0, 0);
     qf[s] = __builtin_bit_cast(bf16x8, w);
   }
 
-  // Keys this workgroup must visit: all of them, or under the causal mask up to the
-  // last key visible from its last valid row.
+  // ---- key blocks to visit
+  const int diag = Nk - Nq;  // key j visible from row i iff j <= i + diag
   int kend = Nk;
-  if (CAUSAL) {
-    const int last_row = min(m0 + kBM, Nq) - 1;
-    kend = min(Nk, last_row + (Nk - Nq) + 1);
+  if (CAUSAL) kend = min(Nk, min(m0 + BM, Nq) - 1 + diag + 1);
+  const int n = (kend + kBN - 1) / kBN;
+
+  // ---- per-lane LDS byte offsets of the MFMA operand reads
+  // K (A of S^T): row kb*32 + l32, logical chunk 2*st + hi.
+  uint32_t koff[D / 16];
+  {
+    const int sk = Swz<D>::k(l32);  // (kb*32 + l32) has the same swizzle for both kb
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+      koff[st] = (uint32_t)(l32 * D * 2 + (((2 * st + hi) ^ sk) * 16));
   }
-  const int n_tiles = (kend + kBN - 1) / kBN;
-
-  // Register staging of one K/V block.
-  constexpr int KCH = kBN * D / 8 / kThreads;  // 16-byte K chunks per thread
-  constexpr int CW = D / 16;                   // V columns per thread (4 keys x CW)
-  constexpr int VCC = D / CW;                  // column chunks per key row (16)
-  const int v_kg = tid / VCC;                  // 4-key group 0..15
-  const int v_cc = tid % VCC;
-  u32x4 kreg[KCH];
-  uint32_t vreg[4][CW / 2];
-
-  auto load_block = [&](int n0) {
+  // V (A of O^T) through transposed reads: in each 16-lane group, lane p points at
+  // row key0 + p/4 and columns d0 + 4*(p%4) .. +3; the group then receives
+  // V[key0 + i][d0 + p] for i = 0..3.
+  uint32_t voff[D / 32];
+  {
+    const int p = lane & 15;
+    const int g = lane >> 4;
+    const int rowl = 4 * hi + (p >> 2);        // row inside the 16-key step (+16u + 8e)
+    const int sv = Swz<D>::v(rowl);            // rows differ by multiples of 4 only
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = i * kThreads + tid;
-      const int key = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (n0 + key < Nk) w = ldg128(Kb + (size_t)(n0 + key) * kv_stride + col);
-      kreg[i] = w;
+    for (int db = 0; db < D / 32; ++db) {
+      const int dcol = 32 * db + 16 * (g & 1) + 4 * (p & 3);
+      voff[db] = (uint32_t)(rowl * D * 2 + (((dcol >> 3) ^ sv) * 16) + (dcol & 7) * 2);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = n0 + v_kg * 4 + r;
-      const uint16_t* src = Vb + (size_t)key * kv_stride + v_cc * CW;
-      if constexpr (CW == 8) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (key < Nk) w = ldg128(src);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) vreg[r][t] = w[t];
-      } else {
-        u32x2 w = {0u, 0u};
-        if (key < Nk) w = *reinterpret_cast<const u32x2*>(src);
-        vreg[r][0] = w[0];
-        vreg[r][1] = w[1];
-      }
-    }
-  };
-
-  auto store_block = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int id = i * kThreads + tid;
-      const int key = id / (D / 8);
-      const int col = (id % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&sm.k[key][col]) = kreg[i];
-    }
-    const int pos = vt_pos(v_kg * 4);
-#pragma unroll
-    for (int cc = 0; cc < CW; ++cc) {
-      const int sh = (cc & 1) * 16;
-      const uint32_t e0 = (vreg[0][cc >> 1] >> sh) & 0xffffu;
-      const uint32_t e1 = (vreg[1][cc >> 1] >> sh) & 0xffffu;
-      const uint32_t e2 = (vreg[2][cc >> 1] >> sh) & 0xffffu;
-      const uint32_t e3 = (vreg[3][cc >> 1] >> sh) & 0xffffu;
-      u32x2 w = {e0 | (e1 << 16), e2 | (e3 << 16)};
-      *reinterpret_cast<u32x2*>(&sm.vt[v_cc * CW + cc][pos]) = w;
-    }
-  };
+  }
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  float m_run = kNegInf;  // running row max, base-2 units
-  float l_run = 0.f;      // this lane's share of the running row sum
+  float m_ref = kNegInf;  // exponent reference (running max, possibly lagging), base 2
+  float l_run = 0.f;      // this lane's share of the row sum of the bf16-rounded weights
+  float l_lse = 0.f;      // ... and of the unrounded weights (for the LSE)
 
-  const int diag = Nk - Nq;  // key j visible from row i iff j <= i + diag
-
-  if (n_tiles > 0) load_block(0);
-  for (int j = 0; j < n_tiles; ++j) {
-    const int n0 = j * kBN;
-    __syncthreads();
-    store_block();
-    __syncthreads();
-    if (j + 1 < n_tiles) load_block(n0 + kBN);
-
-    // S^T = K Q^T for two 32-key halves.
-    f32x16 s[2];
+  // S^T of one block from LDS stage `st_k`.
+  auto qk = [&](const uint16_t* kt, f32x16* s) __attribute__((always_inline)) {
+    const char* kb8 = reinterpret_cast<const char*>(kt);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[kb * 32 + l32][16 * st + 8 * hi]);
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(kb8 + koff[st] + kb * 32 * D * 2);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
       }
     }
+  };
 
-    // Scale into base-2 units; mask the ragged end and the causal diagonal.
+  // Online-softmax step on the scores of block j, then O^T += V^T P^T.
+  auto softmax_pv = [&](f32x16* s, const uint16_t* vt, int j) __attribute__((always_inline)) {
+    const int n0 = j * kBN;
     const bool need_mask = (n0 + kBN > Nk) || (CAUSAL && (n0 + kBN - 1 > m0 + diag));
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] *= c;
     if (need_mask) {
+      const int lim = qrow + diag;  // last visible key of this row
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool dead = (key >= Nk) || (CAUSAL && key > qrow + diag);
+          const bool dead = (key >= Nk) || (CAUSAL && key > lim);
           s[kb][r] = dead ? kNegInf : s[kb][r];
         }
     }
-
-    // Online softmax update ([FA-notes] §4): m_new = max(m_old, block max).
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = xor32_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float rs = 0.f;
+    const float m_blk = mx * c;  // c > 0
+    if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
+      const float m_new = fmaxf(m_ref, m_blk);
+      // 0 on the first block; a row that has seen no visible key yet keeps alpha = 1
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_ref - m_new);
+      l_run *= alpha;
+      l_lse *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+    float ex0 = 0.f, ex1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[kb][r] - m_use);
-        s[kb][r] = p;
-        rs += p;
+        s[kb][r] = fast_exp2(fmaf(s[kb][r], c, neg_m));
+        if (r & 1) ex1 += s[kb][r];
+        else ex0 += s[kb][r];
       }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    l_lse += ex0 + ex1;
 
-    // P^T fragments: 16 keys per MFMA step, eight consecutive score registers each.
+    // P rounded to bf16 for the second product.  O's normaliser adds up exactly those
+    // rounded weights (v_dot2 with (1, 1)), so O = acc / l is a true weighted mean of V
+    // whatever the exponent reference; the LSE uses the unrounded sum above.
     bf16x8 pf[kBN / 16];
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int u = 0; u < kBN / 16; ++u) {
       const int kb = u >> 1;
       const int base = 8 * (u & 1);
       u32x4 w;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(s[kb][base + 2 * t], s[kb][base + 2 * t + 1]);
+      for (int t = 0; t < 4; ++t) {
+        w[t] = pack_bf16x2(s[kb][base + 2 * t], s[kb][base + 2 * t + 1]);
+        if (t & 1) rs1 = sum_bf16x2(w[t], rs1);
+        else rs0 = sum_bf16x2(w[t], rs0);
+      }
       pf[u] = __builtin_bit_cast(bf16x8, w);
     }
-
-    // O^T += V^T P^T.
+    l_run += rs0 + rs1;
+    const __attribute__((address_space(3))) char* vb =
+        (const __attribute__((address_space(3))) char*)(vt);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int u = 0; u < kBN / 16; ++u) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&sm.vt[db * 32 + l32][16 * u + 8 * hi]);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4_t*)(vb + voff[db] + (16 * u) * D * 2));
+        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4_t*)(vb + voff[db] + (16 * u + 8) * D * 2));
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[u], acc[db], 0, 0, 0);
       }
+  };
+
+  // ---- prologue: K(0), V(0), K(1) in flight; S(0)
+  issue_block<D, WAVES, false>(rk, kv_row_bytes, 0, ks[0], wave, lane);
+  issue_block<D, WAVES, true>(rv, kv_row_bytes, 0, vs[0], wave, lane);
+  if (n > 1) issue_block<D, WAVES, false>(rk, kv_row_bytes, kBN, ks[1], wave, lane);
+  f32x16 s_a[2], s_b[2];
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
+  qk(ks[0], s_a);
+
+  // ---- main loop, unrolled by two so the LDS stages and score buffers are fixed
+  auto step = [&](auto stage_c, int j, f32x16* s_cur, f32x16* s_nxt)
+      __attribute__((always_inline)) {
+    constexpr int sc = decltype(stage_c)::value;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's K(j+1), V(j) have landed
+    __syncthreads();                      // ... and everyone's; stage sc of K is free
+    if (j + 2 < n)
+      issue_block<D, WAVES, false>(rk, kv_row_bytes, (j + 2) * kBN, ks[sc], wave, lane);
+    if (j + 1 < n) {
+      issue_block<D, WAVES, true>(rv, kv_row_bytes, (j + 1) * kBN, vs[1 - sc], wave, lane);
+      qk(ks[1 - sc], s_nxt);
+    }
+    softmax_pv(s_cur, vs[sc], j);
+  };
+  for (int j = 0; j < n; j += 2) {
+    step(std::integral_constant<int, 0>{}, j, s_a, s_b);
+    if (j + 1 < n) step(std::integral_constant<int, 1>{}, j + 1, s_b, s_a);
   }
 
-  // Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
+  // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
   const float l_tot = xor32_sum(l_run);
+  const float l_ex = xor32_sum(l_lse);
   const float inv = 1.f / l_tot;
   if (qrow < Nq) {
     float* Orow = O + ((size_t)(b * Nq + qrow) * Hq + hq) * D;
@@ -275,26 +331,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                    acc[db][4 * g + 3] * inv};
         *reinterpret_cast<f32x4*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
       }
-    if (hi == 0) LSE[((size_t)b * Hq + hq) * Nq + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+    if (hi == 0) LSE[((size_t)b * Hq + hq) * Nq + qrow] = (m_ref + fast_log2(l_ex)) * kLn2;
   }
+  (void)NT;
 }
 
-template <int D, bool CAUSAL>
+template <int D, int WAVES, bool CAUSAL>
 hipError_t launch(const PrefillArgs& a, hipStream_t s) {
-  const int n_mblocks = (a.Nq + kBM - 1) / kBM;
+  constexpr int BM = 32 * WAVES;
+  const int n_mblocks = (a.Nq + BM - 1) / BM;
   const long long blocks = (long long)n_mblocks * a.B * a.Hq;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
-                     a.scale * kLog2e, n_mblocks);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, WAVES, CAUSAL>), dim3((unsigned)blocks),
+                     dim3(WAVES * 64), 0, s, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.o,
+                     a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_mblocks);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
-  return a.causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
+  if (a.d == 64) return a.causal ? launch<64, 4, true>(a, s) : launch<64, 4, false>(a, s);
+  return a.causal ? launch<128, 4, true>(a, s) : launch<128, 4, false>(a, s);
 }
 
 }  // namespace fa
