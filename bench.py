@@ -155,10 +155,17 @@ def main():
                              chunk=dcfg.chunk, o=dec["o"], lse=dec["lse"], workspace=dec["ws"])
 
     print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    # At least `warmup` steps and at least half a second of GPU work, so clocks have
+    # ramped up before the timed region even when one step is short.
+    t_w = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_w < 0.5:
         prefill()
         if dec:
             decode()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     K = args.steps

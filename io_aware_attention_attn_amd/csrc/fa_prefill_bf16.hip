@@ -76,27 +76,40 @@ struct Swz {
   }
 };
 
-// Issue the loads of one 64-key block (rows n0.., all D columns) straight into LDS.
-// Each instruction fills 1 KB of LDS in lane order; the global chunk a lane fetches
-// is chosen so the LDS copy ends up swizzled.
-template <int D, int WAVES, bool IS_V>
-__device__ __forceinline__ void issue_block(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, int n0,
-                                            uint16_t* tile, int wave, int lane) {
-  constexpr int CH = D / 8;
-  constexpr int INSTS = kBN * CH / 64;
-  constexpr int PER_WAVE = INSTS / WAVES;
+// Loads of one 64-key block (all D columns) straight into LDS.  Each instruction
+// fills 1 KB of LDS in lane order; the global chunk a lane fetches is chosen so the
+// LDS copy ends up swizzled.  The per-lane byte offsets are fixed (block_offsets);
+// the block's row offset goes in the scalar offset (issue_block).
+template <int D, int WAVES>
+struct BlockShape {
+  static constexpr int CH = D / 8;
+  static constexpr int INSTS = kBN * CH / 64;
+  static constexpr int PER_WAVE = INSTS / WAVES;
   static_assert(PER_WAVE * WAVES == INSTS, "block split");
+};
+
+template <int D, int WAVES, bool IS_V>
+__device__ __forceinline__ void block_offsets(uint32_t* voff, uint32_t row_bytes, int wave,
+                                              int lane) {
+  using S = BlockShape<D, WAVES>;
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int inst = wave * PER_WAVE + i;
-    const int lin = inst * 64 + lane;
-    const int row = lin / CH;
-    const int pos = lin % CH;
+  for (int i = 0; i < S::PER_WAVE; ++i) {
+    const int lin = (wave * S::PER_WAVE + i) * 64 + lane;
+    const int row = lin / S::CH;
+    const int pos = lin % S::CH;
     const int c = pos ^ (IS_V ? Swz<D>::v(row) : Swz<D>::k(row));
-    const uint32_t voff = (uint32_t)(n0 + row) * row_bytes + (uint32_t)c * 16u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + inst * 512), 16, voff, 0, 0,
-                                             0);
+    voff[i] = (uint32_t)row * row_bytes + (uint32_t)c * 16u;
   }
+}
+
+template <int D, int WAVES>
+__device__ __forceinline__ void issue_block(__amdgpu_buffer_rsrc_t rs, const uint32_t* voff,
+                                            uint32_t soff, uint16_t* tile, int wave) {
+  using S = BlockShape<D, WAVES>;
+#pragma unroll
+  for (int i = 0; i < S::PER_WAVE; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_void_t*)(tile + (wave * S::PER_WAVE + i) * 512), 16, voff[i], soff, 0, 0);
 }
 
 __device__ __forceinline__ int xcd_remap(int g, int T) {
@@ -120,7 +133,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -194,43 +207,52 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   float l_run = 0.f;      // this lane's share of the row sum of the bf16-rounded weights
   float l_lse = 0.f;      // ... and of the unrounded weights (for the LSE)
 
-  // S^T of one block from LDS stage `st_k`.
+  uint32_t kvo[BlockShape<D, WAVES>::PER_WAVE], vvo[BlockShape<D, WAVES>::PER_WAVE];
+  block_offsets<D, WAVES, false>(kvo, kv_row_bytes, wave, lane);
+  block_offsets<D, WAVES, true>(vvo, kv_row_bytes, wave, lane);
+
+  // S^T of one block: 16 MFMAs over two independent 32-key accumulators.
   auto qk = [&](const uint16_t* kt, f32x16* s) __attribute__((always_inline)) {
     const char* kb8 = reinterpret_cast<const char*>(kt);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+    for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(kb8 + koff[st] + kb * 32 * D * 2);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb8 + koff[st] + kb * 32 * D * 2);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
       }
-    }
   };
 
-  // Online-softmax step on the scores of block j, then O^T += V^T P^T.
-  auto softmax_pv = [&](f32x16* s, const uint16_t* vt, int j) __attribute__((always_inline)) {
-    const int n0 = j * kBN;
-    const bool need_mask = (n0 + kBN > Nk) || (CAUSAL && (n0 + kBN - 1 > m0 + diag));
-    if (need_mask) {
-      const int lim = qrow + diag;  // last visible key of this row
+  // -inf for keys past the end or (causal) past this row's last visible key.
+  auto mask = [&](f32x16* s, int j) __attribute__((always_inline)) {
+    const int rel = qrow + diag - (j * kBN + 4 * hi);  // last visible key, block-relative
+    const int relk = Nk - 1 - (j * kBN + 4 * hi);        // last existing key, block-relative
+    const int lim = CAUSAL ? min(rel, relk) : relk;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool dead = (key >= Nk) || (CAUSAL && key > lim);
-          s[kb][r] = dead ? kNegInf : s[kb][r];
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + 8 * (r >> 2) + (r & 3);
+        s[kb][r] = (key > lim) ? kNegInf : s[kb][r];
+      }
+  };
+
+  // Block maximum of each row in base-2 units (c > 0).
+  auto row_max = [&](const f32x16* s) __attribute__((always_inline)) {
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = xor32_max(mx);
-    const float m_blk = mx * c;  // c > 0
+    return xor32_max(mx) * c;
+  };
+
+  // Move the exponent reference when a row's block max exceeds it by more than kTau
+  // (online-softmax merge, [FA-notes] §4): old sums and accumulator scale by
+  // exp2(m_old - m_new).  Uniform branch across the wave; rare after the first blocks.
+  auto maybe_rescale = [&](float m_blk) __attribute__((always_inline)) {
     if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
       const float m_new = fmaxf(m_ref, m_blk);
       // 0 on the first block; a row that has seen no visible key yet keeps alpha = 1
@@ -243,23 +265,14 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       m_ref = m_new;
     }
-    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
-    float ex0 = 0.f, ex1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = fast_exp2(fmaf(s[kb][r], c, neg_m));
-        if (r & 1) ex1 += s[kb][r];
-        else ex0 += s[kb][r];
-      }
-    l_lse += ex0 + ex1;
+  };
 
-    // P rounded to bf16 for the second product.  O's normaliser adds up exactly those
-    // rounded weights (v_dot2 with (1, 1)), so O = acc / l is a true weighted mean of V
-    // whatever the exponent reference; the LSE uses the unrounded sum above.
-    bf16x8 pf[kBN / 16];
-    float rs0 = 0.f, rs1 = 0.f;
+  // P = exp2(S*c - m_ref), its bf16 fragments, and both row sums.  O's normaliser
+  // adds up exactly the bf16-rounded weights (v_dot2 with (1, 1)), so O = acc / l is
+  // a true weighted mean of V whatever the reference; the LSE uses the unrounded sum.
+  auto exp_pack = [&](f32x16* s, bf16x8* pf) __attribute__((always_inline)) {
+    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+    float ex0 = 0.f, ex1 = 0.f, rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int u = 0; u < kBN / 16; ++u) {
       const int kb = u >> 1;
@@ -267,19 +280,28 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
       u32x4 w;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        w[t] = pack_bf16x2(s[kb][base + 2 * t], s[kb][base + 2 * t + 1]);
+        const float p0 = fast_exp2(fmaf(s[kb][base + 2 * t], c, neg_m));
+        const float p1 = fast_exp2(fmaf(s[kb][base + 2 * t + 1], c, neg_m));
+        ex0 += p0;
+        ex1 += p1;
+        w[t] = pack_bf16x2(p0, p1);
         if (t & 1) rs1 = sum_bf16x2(w[t], rs1);
         else rs0 = sum_bf16x2(w[t], rs0);
       }
       pf[u] = __builtin_bit_cast(bf16x8, w);
     }
+    l_lse += ex0 + ex1;
     l_run += rs0 + rs1;
+  };
+
+  // O^T += V^T P^T, V^T through transposed LDS reads.
+  auto pv = [&](const uint16_t* vt, const bf16x8* pf) __attribute__((always_inline)) {
     const __attribute__((address_space(3))) char* vb =
         (const __attribute__((address_space(3))) char*)(vt);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int u = 0; u < kBN / 16; ++u)
 #pragma unroll
-      for (int u = 0; u < kBN / 16; ++u) {
+      for (int db = 0; db < D / 32; ++db) {
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (lds_bf16x4_t*)(vb + voff[db] + (16 * u) * D * 2));
         const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -289,32 +311,69 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
       }
   };
 
-  // ---- prologue: K(0), V(0), K(1) in flight; S(0)
-  issue_block<D, WAVES, false>(rk, kv_row_bytes, 0, ks[0], wave, lane);
-  issue_block<D, WAVES, true>(rv, kv_row_bytes, 0, vs[0], wave, lane);
-  if (n > 1) issue_block<D, WAVES, false>(rk, kv_row_bytes, kBN, ks[1], wave, lane);
+  auto need_mask = [&](int j) __attribute__((always_inline)) {
+    return (j * kBN + kBN > Nk) || (CAUSAL && (j * kBN + kBN - 1 > m0 + diag));
+  };
+
+  // ---- prologue: K(0), V(0), K(1) in flight; S(0), its mask and max
+  issue_block<D, WAVES>(rk, kvo, 0, ks[0], wave);
+  issue_block<D, WAVES>(rv, vvo, 0, vs[0], wave);
+  if (n > 1) issue_block<D, WAVES>(rk, kvo, kBN * kv_row_bytes, ks[1], wave);
   f32x16 s_a[2], s_b[2];
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
   qk(ks[0], s_a);
+  if (need_mask(0)) mask(s_a, 0);
+  maybe_rescale(row_max(s_a));
 
-  // ---- main loop, unrolled by two so the LDS stages and score buffers are fixed
-  auto step = [&](auto stage_c, int j, f32x16* s_cur, f32x16* s_nxt)
+  // ---- software pipeline.  Iteration j (scores of block j already masked, their max
+  // folded into the reference):
+  //   phase 1: MFMA S(j+1) = K(j+1) Q^T      | VALU exp2 / pack / sums of block j
+  //   (diagonal or ragged block j+1 only: mask)
+  //   phase 2: MFMA O^T += V(j)^T P(j)^T     | VALU row max of block j+1
+  //   then the (rare) reference move for block j+1.
+  // Each phase is one basic block, so the scheduler can interleave that phase's MFMA
+  // with its VALU work (one wave issues its instructions in order).
+  auto step_next = [&](auto stage_c, int j, f32x16* s_cur, f32x16* s_nxt)
       __attribute__((always_inline)) {
     constexpr int sc = decltype(stage_c)::value;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's K(j+1), V(j) have landed
     __syncthreads();                      // ... and everyone's; stage sc of K is free
     if (j + 2 < n)
-      issue_block<D, WAVES, false>(rk, kv_row_bytes, (j + 2) * kBN, ks[sc], wave, lane);
-    if (j + 1 < n) {
-      issue_block<D, WAVES, true>(rv, kv_row_bytes, (j + 1) * kBN, vs[1 - sc], wave, lane);
-      qk(ks[1 - sc], s_nxt);
-    }
-    softmax_pv(s_cur, vs[sc], j);
+      issue_block<D, WAVES>(rk, kvo, (uint32_t)(j + 2) * kBN * kv_row_bytes, ks[sc], wave);
+    issue_block<D, WAVES>(rv, vvo, (uint32_t)(j + 1) * kBN * kv_row_bytes, vs[1 - sc], wave);
+    bf16x8 pf[kBN / 16];
+    qk(ks[1 - sc], s_nxt);
+    exp_pack(s_cur, pf);
+    // Keep the exp/pack work in this block: without a use here the compiler would sink
+    // it past the mask branch, next to its only consumer, and nothing would overlap.
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pf[0])), "v"(__builtin_bit_cast(u32x4, pf[1])),
+                 "v"(__builtin_bit_cast(u32x4, pf[2])), "v"(__builtin_bit_cast(u32x4, pf[3])));
+    if (need_mask(j + 1)) mask(s_nxt, j + 1);
+    pv(vs[sc], pf);
+    const float m_blk = row_max(s_nxt);
+    maybe_rescale(m_blk);
   };
-  for (int j = 0; j < n; j += 2) {
-    step(std::integral_constant<int, 0>{}, j, s_a, s_b);
-    if (j + 1 < n) step(std::integral_constant<int, 1>{}, j + 1, s_b, s_a);
+  auto step_last = [&](auto stage_c, f32x16* s_cur) __attribute__((always_inline)) {
+    constexpr int sc = decltype(stage_c)::value;
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    bf16x8 pf[kBN / 16];
+    exp_pack(s_cur, pf);
+    pv(vs[sc], pf);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  int j = 0;
+  for (; j + 2 < n; j += 2) {
+    step_next(S0{}, j, s_a, s_b);
+    step_next(S1{}, j + 1, s_b, s_a);
+  }
+  if (j + 1 < n) {
+    step_next(S0{}, j, s_a, s_b);
+    step_last(S1{}, s_b);
+  } else {
+    step_last(S0{}, s_a);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
