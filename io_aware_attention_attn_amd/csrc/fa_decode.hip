@@ -7,165 +7,248 @@
 // (FA-3)", itpe.jackerlab.com, §4 names a dedicated decode kernel.  [FA-notes] =
 // "flash-attn" notes, minjae-portfolio.vercel.app, §4 gives the two-block merge
 // that combines the pieces):
-//   kernel 1, one workgroup per (chunk of `chunk` keys, K/V head, batch): all the
-//     query heads of that K/V head's group attend to the chunk's keys; it writes
-//     the chunk-normalised output O_c and lse_c for each of those heads.  Every
-//     K/V byte of the valid keys is read from HBM exactly once.
+//   kernel 1: for every (batch, K/V head, chunk of `chunk` keys) all the query heads
+//     of that K/V head's group attend to the chunk's keys; it writes the
+//     chunk-normalised output O_c and lse_c of each of those heads.  Every K/V byte
+//     of the valid keys is read from HBM exactly once.
 //   kernel 2, one workgroup per (query head, batch): LSE = M + ln sum_c e^(lse_c - M)
 //     with M = max_c lse_c, O = sum_c e^(lse_c - LSE) O_c.
 //
 // gfx950 mapping of kernel 1
-//   * 256 threads = 4 wave64s; each wave takes 64-key pieces of the chunk and keeps
-//     its own running (m, l, acc); the four waves are merged through LDS at the end.
-//   * Scores S^T = K q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d read
-//     straight from HBM into VGPRs (16-byte loads), B = the group's query heads
-//     (up to 16, zero-padded) held in VGPRs.  The matrix cores are far from busy
-//     here; they are used because the group's 8 query heads make the per-byte
-//     arithmetic too high for plain fp32 VALU at HBM speed.
-//   * O^T = V^T P^T with the same instruction: V is transposed through the wave's
-//     own LDS slice, in the permuted key order in which the score layout hands P
-//     to the second product.
-//   * Keys at or beyond the sequence length are never loaded (zero in registers and
-//     -inf in the scores), so poisoned cache padding cannot leak in.
+//   * Every wave is an independent, persistent worker: the (batch, K/V head,
+//     head group, chunk) items form one list, wave w takes items w, w + W, ...
+//     (W = waves in the grid), and walks each item in 64-key steps with the online
+//     softmax kept in registers.  No barriers, no cross-wave merge.
+//   * Software pipeline over the flattened steps: while step s is computed, K of
+//     step s+1 is already in flight into a second VGPR set and V of step s+1 into
+//     the second half of the wave's LDS slice (buffer_load ... lds).
+//   * Scores S^T = K q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d straight
+//     from the K registers, B = the group's query heads (up to 16, zero-padded).
+//     The matrix cores are far from busy; they are used because the group's query
+//     heads make the per-byte arithmetic too high for plain fp32 VALU at HBM speed.
+//   * O^T = V^T P^T with the same instruction; V^T comes from the row-major V slice
+//     through transposed LDS reads (ds_read_b64_tr_b16), in the key order in which
+//     the score layout hands P to the product.
+//   * Buffer loads clip at the sequence length, so cache rows at or beyond it read
+//     as zeros (and get -inf scores): poisoned padding cannot leak in.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // four independent wave workers per workgroup
 constexpr int kWaves = 4;
-constexpr int kSub = 64;   // keys per wave piece
-constexpr int kVPad = 8;   // bf16 padding per transposed V row
+constexpr int kStep = 64;      // keys per step
 
-// Position of 4-key run starting at key kk (multiple of 4, 0..63) in a transposed
-// V row.  Inside each 32-key half, lane group g of the score layout holds keys
-// 4g..4g+3 of the first 16 and of the second 16; the P fragment slots 8g..8g+7
-// take them in that order, so runs are stored 0,4,1,5,2,6,3,7 (by run index).
-__device__ __forceinline__ int dvt_pos(int kk) {
-  const int half = kk >> 5;
-  const int sub = (kk & 31) >> 2;
-  return half * 32 + (sub & 3) * 8 + (sub >> 2) * 4;
+typedef __attribute__((address_space(3))) void dlds_void_t;
+typedef __bf16 dbf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dbf16x4 dlds_bf16x4_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dmake_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
+
+// XOR swizzle of the 16-byte chunk index in a V row: a half-wave's transposed read
+// touches 8 consecutive rows x 2 adjacent chunks, which then fall in distinct banks.
+template <int D>
+__device__ __forceinline__ int dswz(int row) {
+  return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3);
+}
+
+// One work item: (batch b, K/V head kvh, head group qg, chunk) -> keys [c0, c1).
+struct Item {
+  int b, kvh, qg, c0, c1;
+};
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint16_t* __restrict__ Qd, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int* __restrict__ seqlens, float* __restrict__ part_o,
-    float* __restrict__ part_lse, int Hq, int Hkv, int Nk_max, int chunk, int max_chunks,
-    int n_qgroups, float c) {
-  constexpr int VT_BYTES = kWaves * D * (kSub + kVPad) * 2;
-  constexpr int MERGE_BYTES = kWaves * 16 * (D + 4) * 4 + 3 * kWaves * 16 * 4;
-  constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+    float* __restrict__ part_lse, int B, int Hq, int Hkv, int Nk_max, int chunk, int max_chunks,
+    int QG, float c) {
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int VI = kStep * CH / 64;    // LDS-direct instructions per step
+  constexpr int DB = D / 16;             // 16-row d blocks of O^T
+  constexpr int KS = D / 32;             // 32-wide d steps of the score product
+  // One array per stage: the compiler's wait insertion can then tell the LDS-DMA
+  // prefetch into one stage from the reads of the other and does not stall on it.
+  __shared__ __attribute__((aligned(1024))) uint16_t vst0[kWaves][kStep * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vst1[kWaves][kStep * D];
 
-  const int chunk_id = blockIdx.x;
-  const int kvh = blockIdx.y / n_qgroups;
-  const int qg = blockIdx.y % n_qgroups;
-  const int b = blockIdx.z;
-  int L = seqlens[b];
-  L = L < 0 ? 0 : (L > Nk_max ? Nk_max : L);
-  const int c0 = chunk_id * chunk;
-  if (c0 >= L) return;  // uniform across the workgroup
-  const int c1 = min(c0 + chunk, L);
-
-  const int G = Hq / Hkv;
-  const int hq0 = kvh * G + qg * 16;
-  const int nq = min(16, G - qg * 16);  // query heads handled here
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15;
-  const int grp = lane >> 4;
+  const int g = lane >> 4;
+  const int G = Hq / Hkv;
+  const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
+  const int per_batch_group = Hkv * QG;
 
-  const size_t kv_stride = (size_t)Hkv * D;
-  const uint16_t* Kb = Kc + ((size_t)b * Nk_max * Hkv + kvh) * D;
-  const uint16_t* Vb = Vc + ((size_t)b * Nk_max * Hkv + kvh) * D;
-
-  // q^T fragments: lane holds query head hq0 + l16, d = 32*s + 8*grp .. +7.
-  bf16x8 qf[D / 32];
+  // ---- per-lane fixed offsets
+  // K fragment (A of S^T): key 16*kb + l16 of the step, d = 32*st + 8*g.
+  const uint32_t k_lane = (uint32_t)l16 * row_bytes + 16u * g;
+  // V LDS-direct: instruction i covers rows (64*i + lane) / CH; the row offset part
+  // that grows with i goes in the scalar offset.
+  uint32_t v_lane[2];
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (l16 < nq) w = ldg128(Qd + ((size_t)b * Hq + hq0 + l16) * D + 32 * s + 8 * grp);
-    qf[s] = __builtin_bit_cast(bf16x8, w);
+  for (int e = 0; e < 2; ++e) {
+    const int lin = e * 64 + lane;
+    const int row = lin / CH;
+    const int pos = lin % CH;
+    v_lane[e] = (uint32_t)row * row_bytes + (uint32_t)((pos ^ dswz<D>(row)) * 16);
+  }
+  // Transposed V reads: in 16-lane group g, lane p points at row 32u + 4g + p/4 (+16
+  // for the second half of the slots) and columns 16*db + 4*(p%4); the group receives
+  // V[row0 + i][16*db + p], i = 0..3.
+  uint32_t tr_off[DB];
+  {
+    const int rowl = 4 * g + (l16 >> 2);
+    const int sw = dswz<D>(rowl);  // rows differ from rowl by multiples of 16 only
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 16 * db + 4 * (l16 & 3);
+      tr_off[db] = (uint32_t)(rowl * D * 2 + (((col >> 3) ^ sw) * 16) + (col & 7) * 2);
+    }
   }
 
-  uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * D * (kSub + kVPad);
+  // ---- item list walk (items ordered batch-major, then chunk, K/V head, head group)
+  const int stride = gridDim.x * kWaves;
+  int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wave);
+  int cb = 0, cbase = 0;               // current batch and its first item index
+  // Sequence lengths are read with scalar loads (constant address space, uniform
+  // index): they complete on their own counter, so reading one never waits for the
+  // vector loads already in flight.
+  const __attribute__((address_space(4))) int* sl =
+      (const __attribute__((address_space(4))) int*)seqlens;
+  // For up to 64 sequences the lengths are also kept one per lane, so a lookup is a
+  // register read instead of a memory round trip at every item change.
+  const int sl_lane = (B <= 64 && lane < B) ? sl[lane] : 0;
+  auto seqlen = [&](int bb) __attribute__((always_inline)) {
+    const int ub = __builtin_amdgcn_readfirstlane(bb);
+    int L = (B <= 64) ? __builtin_amdgcn_readlane(sl_lane, ub) : sl[ub];
+    L = L < 0 ? 0 : (L > Nk_max ? Nk_max : L);
+    return __builtin_amdgcn_readfirstlane(L);
+  };
+  auto locate = [&](int tt, Item& it) __attribute__((always_inline)) -> bool {
+    while (cb < B) {
+      const int n = ((seqlen(cb) + chunk - 1) / chunk) * per_batch_group;
+      if (tt < cbase + n) break;
+      cbase += n;
+      ++cb;
+    }
+    if (cb >= B) return false;
+    const int L = seqlen(cb);
+    const int r = tt - cbase;
+    const int ci = r / per_batch_group;
+    const int rem = r % per_batch_group;
+    it.b = __builtin_amdgcn_readfirstlane(cb);
+    it.kvh = __builtin_amdgcn_readfirstlane(rem / QG);
+    it.qg = __builtin_amdgcn_readfirstlane(rem % QG);
+    it.c0 = __builtin_amdgcn_readfirstlane(ci * chunk);
+    it.c1 = __builtin_amdgcn_readfirstlane(min(ci * chunk + chunk, L));
+    return true;
+  };
 
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{};
-  // l_run sums the bf16-rounded weights (O's normaliser), l_lse the unrounded ones.
+  Item cur, nxt;
+  if (!locate(t, cur)) return;
+  int cur_n0 = cur.c0;
+
+  u32x4 kA[4][KS], kB[4][KS];  // two VGPR sets of K fragments
+  bf16x8 qf[KS];
+  f32x4 acc[DB];
   float m_run = kNegInf, l_run = 0.f, l_lse = 0.f;
 
-  // V loading: a lane owns column chunk vcc (8 d) of 4-key runs kq, kq+KQ, ...
-  constexpr int CPR = D / 8;          // 16-byte chunks per key row
-  constexpr int KQ = 64 / CPR;        // lanes per column chunk (4 or 8)
-  constexpr int RUNS = 16 / KQ;       // 4-key runs per lane (4 or 2)
-  const int vcc = lane % CPR;
-  const int vkq = lane / CPR;
+  // Buffer descriptors of one item's K or V slice, clipped after key c1 - 1.  Built
+  // from values forced into scalar registers so the loads need no per-lane loop.
+  auto rsrc_of = [&](const uint16_t* base, const Item& it) __attribute__((always_inline)) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base + ((size_t)it.b * Nk_max * Hkv + it.kvh) * D);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)(it.c1 - 1) * row_bytes + D * 2);
+    return dmake_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nrec);
+  };
+  // Issue the loads of the step at key n0 of item `it`: K into `kf`, V into LDS stage.
+  auto issue = [&](const Item& it, int n0, u32x4 (*kf)[KS], auto stage_c)
+      __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_c)::value;
+    const __amdgpu_buffer_rsrc_t rk = rsrc_of(Kc, it);
+    const __amdgpu_buffer_rsrc_t rv = rsrc_of(Vc, it);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        kf[kb][st] = __builtin_amdgcn_raw_buffer_load_b128(
+            rk, k_lane + 64u * st, (uint32_t)(n0 + 16 * kb) * row_bytes, 0);
+    uint16_t* dst = stage == 1 ? vst1[wave] : vst0[wave];
+#pragma unroll
+    for (int i = 0; i < VI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (dlds_void_t*)(dst + i * 512), 16, v_lane[i & 1],
+          (uint32_t)n0 * row_bytes + (uint32_t)(i & ~1) * (64 / CH) * row_bytes, 0, 0);
+  };
 
-  for (int n0 = c0 + wave * kSub; n0 < c1; n0 += kWaves * kSub) {
-    // K fragments straight from HBM, V rows into registers.
-    u32x4 kf[4][D / 32];
+  auto item_begin = [&](const Item& it) __attribute__((always_inline)) {
+    const int hq0 = it.kvh * G + it.qg * 16;
+    const int nq = min(16, G - it.qg * 16);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = n0 + kb * 16 + l16;
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (key < c1) w = ldg128(Kb + (size_t)key * kv_stride + 32 * s + 8 * grp);
-        kf[kb][s] = w;
-      }
+    for (int st = 0; st < KS; ++st) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (l16 < nq) w = ldg128(Qd + ((size_t)it.b * Hq + hq0 + l16) * D + 32 * st + 8 * g);
+      qf[st] = __builtin_bit_cast(bf16x8, w);
     }
-    u32x4 vr[RUNS][4];
 #pragma unroll
-    for (int ru = 0; ru < RUNS; ++ru)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = n0 + (vkq + ru * KQ) * 4 + r;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (key < c1) w = ldg128(Vb + (size_t)key * kv_stride + vcc * 8);
-        vr[ru][r] = w;
-      }
+    for (int i = 0; i < DB; ++i) acc[i] = f32x4{};
+    m_run = kNegInf;
+    l_run = 0.f;
+    l_lse = 0.f;
+  };
 
-    // Transpose V into this wave's LDS slice.
+  auto item_end = [&](const Item& it) __attribute__((always_inline)) {
+    float lr = l_run, le = l_lse;
+    lr += __shfl_xor(lr, 16);
+    lr += __shfl_xor(lr, 32);
+    le += __shfl_xor(le, 16);
+    le += __shfl_xor(le, 32);
+    const int hq0 = it.kvh * G + it.qg * 16;
+    const int nq = min(16, G - it.qg * 16);
+    if (l16 < nq) {
+      const int hq = hq0 + l16;
+      const int ci = it.c0 / chunk;
+      const float inv = 1.f / lr;
+      float* dst = part_o + (((size_t)it.b * Hq + hq) * max_chunks + ci) * D;
 #pragma unroll
-    for (int ru = 0; ru < RUNS; ++ru) {
-      const int pos = dvt_pos((vkq + ru * KQ) * 4);
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        const int sh = (cc & 1) * 16;
-        const uint32_t e0 = (vr[ru][0][cc >> 1] >> sh) & 0xffffu;
-        const uint32_t e1 = (vr[ru][1][cc >> 1] >> sh) & 0xffffu;
-        const uint32_t e2 = (vr[ru][2][cc >> 1] >> sh) & 0xffffu;
-        const uint32_t e3 = (vr[ru][3][cc >> 1] >> sh) & 0xffffu;
-        u32x2 w = {e0 | (e1 << 16), e2 | (e3 << 16)};
-        *reinterpret_cast<u32x2*>(&vt[(vcc * 8 + cc) * (kSub + kVPad) + pos]) = w;
-      }
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = acc[db] * inv;
+      if (g == 0)
+        part_lse[((size_t)it.b * Hq + hq) * max_chunks + ci] = (m_run + fast_log2(le)) * kLn2;
     }
+  };
 
-    // S^T = K q^T: four 16-key blocks.
+  // One 64-key step: scores, online softmax, P V.
+  auto compute = [&](const Item& it, int n0, u32x4 (*kf)[KS], auto stage_c)
+      __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_c)::value;
     f32x4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       s[kb] = f32x4{};
 #pragma unroll
-      for (int st = 0; st < D / 32; ++st)
+      for (int st = 0; st < KS; ++st)
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kb][st]),
                                                         qf[st], s[kb], 0, 0, 0);
     }
     float mx = kNegInf;
+    const int lim = it.c1 - 1 - (n0 + 4 * g);  // last valid key, relative to this lane's keys
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = n0 + kb * 16 + 4 * grp + r;
-        const float t = (key < c1) ? s[kb][r] * c : kNegInf;
-        s[kb][r] = t;
-        mx = fmaxf(mx, t);
+        const float tv = (kb * 16 + r > lim) ? kNegInf : s[kb][r] * c;
+        s[kb][r] = tv;
+        mx = fmaxf(mx, tv);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -180,13 +263,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         s[kb][r] = fast_exp2(s[kb][r] - m_use);
         ex += s[kb][r];
       }
-    l_lse = l_lse * alpha + ex;
     m_run = m_new;
+    l_lse = l_lse * alpha + ex;
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
-
-    // P rounded to bf16 for the second product; the row sum adds those same rounded
-    // weights, so the chunk output is a true weighted mean of V.
+    for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+    // P rounded to bf16 for the second product; the row sum for O adds those same
+    // rounded weights, so the chunk output is a true weighted mean of V.
     bf16x8 pf[2];
     float rs = 0.f;
 #pragma unroll
@@ -195,125 +277,181 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
                  pack_bf16x2(s[2 * u + 1][0], s[2 * u + 1][1]),
                  pack_bf16x2(s[2 * u + 1][2], s[2 * u + 1][3])};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) rs = sum_bf16x2(w[t], rs);
+      for (int q4 = 0; q4 < 4; ++q4) rs = sum_bf16x2(w[q4], rs);
       pf[u] = __builtin_bit_cast(bf16x8, w);
     }
     l_run = l_run * alpha + rs;
-    // The wave's own LDS writes must land before its lanes read each other's data.
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
+    const __attribute__((address_space(3))) char* vb =
+        (const __attribute__((address_space(3))) char*)(stage == 1 ? vst1[wave] : vst0[wave]);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &vt[(db * 16 + l16) * (kSub + kVPad) + 32 * u + 8 * grp]);
+      for (int db = 0; db < DB; ++db) {
+        const dbf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (dlds_bf16x4_t*)(vb + tr_off[db] + (32 * u) * D * 2));
+        const dbf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (dlds_bf16x4_t*)(vb + tr_off[db] + (32 * u + 16) * D * 2));
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[u], acc[db], 0, 0, 0);
       }
-    __builtin_amdgcn_wave_barrier();
-  }
+  };
 
-  // Row sums across the four lane groups that share a query.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  l_lse += __shfl_xor(l_lse, 16);
-  l_lse += __shfl_xor(l_lse, 32);
-
-  // Merge the four waves through LDS (the V slices are dead by now).
-  __syncthreads();
-  float* mo = reinterpret_cast<float*>(smem);                 // [4][16][D+4]
-  float* mm = mo + kWaves * 16 * (D + 4);                     // [4][16]
-  float* ml = mm + kWaves * 16;                               // [4][16]
-  float* mle = ml + kWaves * 16;                              // [4][16]
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-    *reinterpret_cast<f32x4*>(&mo[(wave * 16 + l16) * (D + 4) + db * 16 + 4 * grp]) = acc[db];
-  if (grp == 0) {
-    mm[wave * 16 + l16] = m_run;
-    ml[wave * 16 + l16] = l_run;
-    mle[wave * 16 + l16] = l_lse;
-  }
-  __syncthreads();
-
-  constexpr int TPQ = kThreads / 16;  // threads per query head (16)
-  constexpr int DPT = D / TPQ;        // d per thread (8 or 4)
-  const int qi = tid / TPQ;
-  const int d0 = (tid % TPQ) * DPT;
-  if (qi < nq) {
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * 16 + qi]);
-    float wsc[kWaves];
-    float Lsum = 0.f, Lex = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      wsc[w] = fast_exp2(mm[w * 16 + qi] - M);  // 0 for a wave that saw no key
-      Lsum += wsc[w] * ml[w * 16 + qi];
-      Lex += wsc[w] * mle[w * 16 + qi];
+  // Next step after (it, n0): the next 64 keys of the item, or the first step of the
+  // wave's next item.  Returns false when the wave has no more work.
+  auto advance = [&](const Item& it, int n0, Item& nit, int& nn0)
+      __attribute__((always_inline)) -> bool {
+    if (n0 + kStep < it.c1) {
+      nit = it;
+      nn0 = __builtin_amdgcn_readfirstlane(n0 + kStep);
+      return true;
     }
-    const float inv = 1.f / Lsum;
-    const int hq = hq0 + qi;
-    float* dst = part_o + (((size_t)b * Hq + hq) * max_chunks + chunk_id) * D + d0;
-#pragma unroll
-    for (int i = 0; i < DPT; i += 4) {
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&mo[(w * 16 + qi) * (D + 4) + d0 + i]);
-        o += x * wsc[w];
-      }
-      *reinterpret_cast<f32x4*>(dst + i) = o * inv;
+    t = __builtin_amdgcn_readfirstlane(t + stride);
+    if (!locate(t, nit)) return false;
+    nn0 = nit.c0;
+    return true;
+  };
+
+  // ---- software pipeline, unrolled by two for the two K register sets / LDS stages
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  item_begin(cur);
+  issue(cur, cur_n0, kA, S0{});
+  auto half = [&](u32x4 (*kc)[KS], u32x4 (*kn)[KS], auto stage_c, auto other_c)
+      __attribute__((always_inline)) -> bool {
+    int nn0 = 0;
+    const bool more = advance(cur, cur_n0, nxt, nn0);
+    if (more) {
+      issue(nxt, nn0, kn, other_c);
+      // wait for this step's loads: everything but the just-issued 4*KS + VI
+      static_assert(4 * KS + VI == 32 || 4 * KS + VI == 16, "vmcnt encoding");
+      if constexpr (4 * KS + VI == 32) __builtin_amdgcn_s_waitcnt(0x8f70);  // vmcnt(32)
+      else __builtin_amdgcn_s_waitcnt(0x4f70);                             // vmcnt(16)
+      compute(cur, cur_n0, kc, stage_c);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      compute(cur, cur_n0, kc, stage_c);
     }
-    if (d0 == 0)
-      part_lse[((size_t)b * Hq + hq) * max_chunks + chunk_id] = (M + fast_log2(Lex)) * kLn2;
+    const bool new_item = !more || nn0 == nxt.c0 && (nxt.b != cur.b || nxt.kvh != cur.kvh ||
+                                                      nxt.qg != cur.qg || nxt.c0 != cur.c0);
+    if (new_item) {
+      item_end(cur);
+      if (more) item_begin(nxt);
+    }
+    cur = nxt;
+    cur_n0 = nn0;
+    return more;
+  };
+  while (true) {
+    if (!half(kA, kB, S0{}, S1{})) break;
+    if (!half(kB, kA, S1{}, S0{})) break;
   }
 }
 
-// Kernel 2: merge the chunks of one (query head, batch).  One thread per d column.
+// Kernel 2: merge the chunks of one (query head, batch).  The four waves take every
+// fourth chunk; each lane owns D/64 columns.  Per wave: running maximum, weights and
+// weighted sums with several chunk rows in flight; the four partial results are then
+// combined through LDS with the same merge rule.
+constexpr int kMergeThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const int* __restrict__ seqlens,
-                                                         const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_lse,
-                                                         float* __restrict__ O,
-                                                         float* __restrict__ LSE, int Hq,
-                                                         int Nk_max, int chunk, int max_chunks) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
+    const int* __restrict__ seqlens, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse, float* __restrict__ O, float* __restrict__ LSE, int Hq,
+    int Nk_max, int chunk, int max_chunks) {
+  constexpr int W = kMergeThreads / 64;
+  constexpr int DPL = D / 64;  // columns per lane
+  __shared__ float s_m[W], s_l[W];
+  __shared__ float s_acc[W][D];
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   int L = seqlens[b];
   L = L < 0 ? 0 : (L > Nk_max ? Nk_max : L);
   const int nc = (L + chunk - 1) / chunk;
   const size_t row = (size_t)b * Hq + hq;
   const float* pl = part_lse + row * max_chunks;
-  const float* po = part_o + row * max_chunks * D + d;
+  const float* po = part_o + row * max_chunks * D + lane * DPL;
 
+  // Wave-level maximum over this wave's chunks (every lane reads the same lse values).
   float M = kNegInf;
-  for (int ci = 0; ci < nc; ++ci) M = fmaxf(M, pl[ci]);
-  float ssum = 0.f, acc = 0.f;
-  for (int ci = 0; ci < nc; ++ci) {
-    const float w = fast_exp2((pl[ci] - M) * kLog2e);
-    ssum += w;
-    acc = fmaf(w, po[(size_t)ci * D], acc);
+  for (int ci = wave; ci < nc; ci += W) M = fmaxf(M, pl[ci]);
+  float ssum = 0.f;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  const float Mref = (M == kNegInf) ? 0.f : M;
+  int ci = wave;
+  for (; ci + 3 * W < nc; ci += 4 * W) {  // four chunk rows in flight
+    float lv[4], ov[4][DPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lv[u] = pl[ci + u * W];
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) ov[u][i] = po[(size_t)(ci + u * W) * D + i];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = fast_exp2((lv[u] - Mref) * kLog2e);
+      ssum += w;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, ov[u][i], acc[i]);
+    }
   }
-  O[row * D + d] = (nc > 0) ? acc / ssum : 0.f;
-  if (d == 0) LSE[row] = (nc > 0) ? M + fast_log2(ssum) * kLn2 : kNegInf;
+  for (; ci < nc; ci += W) {
+    const float w = fast_exp2((pl[ci] - Mref) * kLog2e);
+    ssum += w;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, po[(size_t)ci * D + i], acc[i]);
+  }
+  if (lane == 0) {
+    s_m[wave] = M;
+    s_l[wave] = ssum;
+  }
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) s_acc[wave][lane * DPL + i] = acc[i];
+  __syncthreads();
+
+  // Combine the four waves (a wave that had no chunk contributes weight 0).
+  float Mt = kNegInf;
+#pragma unroll
+  for (int w = 0; w < W; ++w) Mt = fmaxf(Mt, s_m[w]);
+  const float Mtr = (Mt == kNegInf) ? 0.f : Mt;
+  float wsc[W], St = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    wsc[w] = (s_m[w] == kNegInf) ? 0.f : fast_exp2((s_m[w] - Mtr) * kLog2e);
+    St += wsc[w] * s_l[w];
+  }
+  for (int d = threadIdx.x; d < D; d += kMergeThreads) {
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) o = fmaf(wsc[w], s_acc[w][d], o);
+    O[row * D + d] = (nc > 0) ? o / St : 0.f;
+  }
+  if (threadIdx.x == 0) LSE[row] = (nc > 0) ? Mtr + fast_log2(St) * kLn2 : kNegInf;
 }
 
 template <int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const int n_qgroups = (G + 15) / 16;
-  hipLaunchKernelGGL((decode_split_kernel<D>),
-                     dim3((unsigned)a.max_chunks, (unsigned)(a.Hkv * n_qgroups), (unsigned)a.B),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t*>(a.q),
-                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                     a.seqlens, a.part_o, a.part_lse, a.Hq, a.Hkv, a.Nk_max, a.chunk,
-                     a.max_chunks, n_qgroups, a.scale * kLog2e);
+  const int QG = (G + 15) / 16;
+  // Persistent wave workers: one workgroup (4 workers, 128 KB of LDS) per CU.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+  }
+  hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)cus), dim3(kThreads), 0, s,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.seqlens, a.part_o, a.part_lse, a.B,
+                     a.Hq, a.Hkv, a.Nk_max, a.chunk, a.max_chunks, QG, a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(D), 0, s,
-                     a.seqlens, a.part_o, a.part_lse, a.o, a.lse, a.Hq, a.Nk_max, a.chunk,
-                     a.max_chunks);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.Hq, (unsigned)a.B),
+                     dim3(kMergeThreads), 0, s, a.seqlens, a.part_o, a.part_lse, a.o, a.lse,
+                     a.Hq, a.Nk_max, a.chunk, a.max_chunks);
   return hipGetLastError();
 }
 

@@ -128,8 +128,15 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int BM = 32 * WAVES;
   constexpr int NT = WAVES * 64;
-  __shared__ __attribute__((aligned(1024))) uint16_t ks[2][kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs[2][kBN * D];
+  // One array per stage: the compiler's wait insertion can then tell an LDS-DMA
+  // write into one stage from reads of the other, and does not stall the reads of
+  // the current block on the prefetch of the next one.
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs1[kBN * D];
+  uint16_t* const ks[2] = {ks0, ks1};
+  uint16_t* const vs[2] = {vs0, vs1};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
