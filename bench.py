@@ -48,6 +48,25 @@ def parse():
     return ap.parse_args()
 
 
+def profiled_traffic(kernel: str):
+    """HBM bytes per dispatch of `kernel` from profiles/hbm_traffic.json (rocprofv3 FETCH_SIZE
+    and WRITE_SIZE, copy-calibrated), or None when the kernel's sources changed since then."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[kernel]
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return rec["traffic_bytes"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def copy_calib():
     import torch
     n = 1 << 30
@@ -213,7 +232,10 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, causal>",
                      "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": (profiled_traffic("prefill_bf16_kernel<128, 4, true>")
+                                 if pcfg.d == 128 and pcfg.causal else None),
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "avg_launch_ms": round(avg_pre, 4),
                      "flop_per_launch": flops},
         "wall_s_timed_region": round(wall, 3),
@@ -228,7 +250,9 @@ def main():
                             "avg_call_ms": round(avg_dec, 4),
                             "kernels": "split + merge (one call)",
                             "bytes_per_call": dbytes,
-                            "sum_seqlens": int(dec["lengths"].sum().item())}
+                            "sum_seqlens": int(dec["lengths"].sum().item()),
+                            "traffic_split": profiled_traffic("decode_split_kernel<128>"),
+                            "traffic_merge": profiled_traffic("decode_merge_kernel<128>")}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_prefill(pcfg, args.cpu_seconds)

@@ -22,7 +22,7 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers, contiguous, row-major, 16-byte
- *     aligned.  The caller owns every buffer; the library allocates nothing,
+ *     aligned (the decode LSE output and seqlens_k need only 4-byte alignment).  The caller owns every buffer; the library allocates nothing,
  *     keeps no state and never synchronises.  Work is enqueued on `stream`
  *     (NULL = the default stream) and the call returns right after the launch.
  *   - Arguments are validated on the host before any HIP call; a negative
@@ -41,6 +41,8 @@
  *     Nq == Nk this is "token i sees tokens 0..i").  causal with Nq > Nk is
  *     rejected because some rows would see no key at all.
  *   - d (head dimension) must be 64 or 128.
+ *   - Sizes: every (batch) slice of Q, K and V must stay below 2^31 bytes, and the
+ *     grid is one-dimensional (FA_ERR_SHAPE otherwise).
  *   - Thread safety: every function may be called concurrently from several
  *     host threads; calls on one stream execute in stream order.
  */
