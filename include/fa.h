@@ -104,8 +104,9 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
 
 /*
  * fa_decode_splitkv_workspace_bytes — bytes of device workspace that
- * fa_decode_splitkv needs for these sizes (per-chunk partial outputs and
- * log-sum-exps in fp32).  Returns 0 for invalid sizes.
+ * fa_decode_splitkv needs for these sizes (per-piece partial outputs and
+ * log-sum-exps in fp32, room for ceil(Nk_max / chunk) + 1 pieces per (b, query
+ * head)).  Returns 0 for invalid sizes.
  */
 size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int chunk);
 
@@ -114,12 +115,15 @@ size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int c
  *
  * [LLM-basics] ②-3/②-4: a single new query token per sequence attends to all
  * of that sequence's cached keys and values; [FA3-entry] §4 names a dedicated
- * decode kernel.  The keys of sequence b are cut into chunks of `chunk` keys;
- * kernel 1 computes, for every (b, K/V head, chunk), the attention of all
- * Hq/Hkv query heads of that group to the chunk's keys: the chunk-normalised
- * output O_c and lse_c.  Kernel 2 merges the chunks of each (b, query head)
- * with the two-block online-softmax merge of [FA-notes] §4 applied across all
- * chunks: LSE = M + ln sum_c exp(lse_c - M), O = sum_c exp(lse_c - LSE) O_c.
+ * decode kernel.  The keys of every (b, K/V head) are cut into pieces; kernel 1
+ * computes, for every piece, the attention of all Hq/Hkv query heads of that
+ * group to the piece's keys: the piece-normalised output O_p and lse_p.  The
+ * pieces come from splitting all (b, K/V head) key ranges, laid end to end, into
+ * equal runs, one per wave of the GPU, so every wave streams the same number of
+ * bytes whatever the length mix; a run is at least `chunk` keys.  Kernel 2
+ * merges the pieces of each (b, query head) with the two-block online-softmax
+ * merge of [FA-notes] §4 applied across all pieces:
+ * LSE = M + ln sum_p exp(lse_p - M), O = sum_p exp(lse_p - LSE) O_p.
  *
  *   q          bf16  [B, Hq, d]             (read)
  *   k_cache    bf16  [B, Nk_max, Hkv, d]    (read; rows >= seqlens_k[b] are never read)
@@ -129,7 +133,8 @@ size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int c
  *              a sequence with 0 keys gets O = 0 and LSE = -inf.
  *   o          fp32  [B, Hq, d]             (written)
  *   lse        fp32  [B, Hq]                (written)
- *   chunk      keys per split, a positive multiple of 64 (256 for the standard setup)
+ *   chunk      smallest run of keys one wave takes, a positive multiple of 64 (256 for
+ *              the standard setup); it bounds the number of pieces and so the workspace
  *   workspace  device buffer of at least fa_decode_splitkv_workspace_bytes(...)
  *              bytes, 16-byte aligned, owned by the caller; its contents on entry
  *              do not matter and are overwritten.

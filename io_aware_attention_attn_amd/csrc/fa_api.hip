@@ -31,7 +31,14 @@ int check_prefill(const void* q, const void* k, const void* v, const float* o, c
   return FA_OK;
 }
 
-int max_chunks_of(int Nk_max, int chunk) { return (Nk_max + chunk - 1) / chunk; }
+// Most pieces one (batch, K/V head) of the decode can be cut into: its steps of 64 keys
+// are split over consecutive waves in runs of at least chunk / 64 steps, and a run
+// boundary can fall on either side of the segment.
+int max_pieces_of(int Nk_max, int chunk) {
+  const int steps = (Nk_max + 63) / 64;
+  const int rmin = chunk / 64;
+  return (steps + rmin - 1) / rmin + 1;
+}
 
 int check_decode_sizes(int B, int Hq, int Hkv, int Nk_max, int d, int chunk) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nk_max <= 0 || d <= 0) return FA_ERR_SHAPE;
@@ -39,10 +46,11 @@ int check_decode_sizes(int B, int Hq, int Hkv, int Nk_max, int d, int chunk) {
   if ((long long)B * Nk_max * Hkv > INT_MAX) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (chunk <= 0 || chunk % 64 != 0) return FA_ERR_UNSUPPORTED;
-  const long long mc = max_chunks_of(Nk_max, chunk);
   const long long G = Hq / Hkv;
-  if (mc > 0x7fffffffLL || (long long)Hkv * ((G + 15) / 16) > 65535 || B > 65535)
-    return FA_ERR_SHAPE;
+  // the split kernel counts all 64-key steps of all (batch, K/V head, head group)
+  // segments in 32-bit integers; Hkv * ceil(G / 16) <= Hq bounds the segment count
+  const long long steps = (long long)B * Hq * ((Nk_max + 63) / 64);
+  if (steps > 0x3fffffffLL || Hq > 65535 || B > 65535) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -69,8 +77,8 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
 
 size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int chunk) {
   if (check_decode_sizes(B, Hq, 1, Nk_max, d, chunk) != FA_OK) return 0;
-  const int mc = max_chunks_of(Nk_max, chunk);
-  return fa::decode_part_o_bytes(B, Hq, mc, d) + fa::decode_part_lse_bytes(B, Hq, mc);
+  const int mp = max_pieces_of(Nk_max, chunk);
+  return fa::decode_part_o_bytes(B, Hq, mp, d) + fa::decode_part_lse_bytes(B, Hq, mp);
 }
 
 int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
@@ -83,15 +91,15 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(o) ||
       (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return FA_ERR_ALIGN;
-  const int mc = max_chunks_of(Nk_max, chunk);
-  const size_t need = fa::decode_part_o_bytes(B, Hq, mc, d) + fa::decode_part_lse_bytes(B, Hq, mc);
+  const int mp = max_pieces_of(Nk_max, chunk);
+  const size_t need = fa::decode_part_o_bytes(B, Hq, mp, d) + fa::decode_part_lse_bytes(B, Hq, mp);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (misaligned(workspace)) return FA_ERR_ALIGN;
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             fa::decode_part_o_bytes(B, Hq, mc, d));
+                                             fa::decode_part_o_bytes(B, Hq, mp, d));
   fa::DecodeArgs a{q, k_cache, v_cache, seqlens_k, o, lse, part_o, part_lse,
-                   B, Hq, Hkv, Nk_max, d, chunk, mc, scale};
+                   B, Hq, Hkv, Nk_max, d, chunk, mp, scale};
   return fa::launch_decode_splitkv(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

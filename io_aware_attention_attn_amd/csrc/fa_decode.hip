@@ -7,21 +7,24 @@
 // (FA-3)", itpe.jackerlab.com, §4 names a dedicated decode kernel.  [FA-notes] =
 // "flash-attn" notes, minjae-portfolio.vercel.app, §4 gives the two-block merge
 // that combines the pieces):
-//   kernel 1: for every (batch, K/V head, chunk of `chunk` keys) all the query heads
-//     of that K/V head's group attend to the chunk's keys; it writes the
-//     chunk-normalised output O_c and lse_c of each of those heads.  Every K/V byte
-//     of the valid keys is read from HBM exactly once.
-//   kernel 2, one workgroup per (query head, batch): LSE = M + ln sum_c e^(lse_c - M)
-//     with M = max_c lse_c, O = sum_c e^(lse_c - LSE) O_c.
+//   kernel 1: the keys of every (batch, K/V head) are cut into pieces; for each piece
+//     all the query heads of that K/V head's group attend to the piece's keys, and
+//     the piece-normalised output O_p and lse_p of each of those heads are written.
+//     Every K/V byte of the valid keys is read from HBM exactly once.
+//   kernel 2, one workgroup per (query head, batch): LSE = M + ln sum_p e^(lse_p - M)
+//     with M = max_p lse_p, O = sum_p e^(lse_p - LSE) O_p.
 //
 // gfx950 mapping of kernel 1
-//   * Every wave is an independent, persistent worker: the (batch, K/V head,
-//     head group, chunk) items form one list, wave w takes items w, w + W, ...
-//     (W = waves in the grid), and walks each item in 64-key steps with the online
-//     softmax kept in registers.  No barriers, no cross-wave merge.
-//   * Software pipeline over the flattened steps: while step s is computed, K of
-//     step s+1 is already in flight into a second VGPR set and V of step s+1 into
-//     the second half of the wave's LDS slice (buffer_load ... lds).
+//   * Every wave is an independent, persistent worker.  The (batch, K/V head, head
+//     group) segments are laid end to end in 64-key steps, T steps in all, and wave w
+//     takes the contiguous steps [w R, (w+1) R) with R = max(ceil(T / W), chunk / 64)
+//     (W = waves in the grid): every wave streams the same number of bytes whatever
+//     the length mix.  A wave writes one partial result (O_p, lse_p) for each piece of
+//     a segment that its range covers, so a segment of n steps has at most
+//     ceil(n / R) + 1 pieces and the merge reads a few records per query head.
+//   * Software pipeline over the wave's steps: while step s is computed, K of step
+//     s+1 is already in flight into a second VGPR set and V of step s+1 into the
+//     second half of the wave's LDS slice (buffer_load ... lds).
 //   * Scores S^T = K q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d straight
 //     from the K registers, B = the group's query heads (up to 16, zero-padded).
 //     The matrix cores are far from busy; they are used because the group's query
@@ -59,16 +62,24 @@ __device__ __forceinline__ int dswz(int row) {
   return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3);
 }
 
-// One work item: (batch b, K/V head kvh, head group qg, chunk) -> keys [c0, c1).
-struct Item {
-  int b, kvh, qg, c0, c1;
+// Where a wave is: batch b, K/V head kvh, head group qg of segment `seg` (= kvh * QG +
+// qg) of that batch, step i (keys [64 i, 64 i + 64) clipped at the length L, nb steps
+// in the segment), and S, the global index of the segment's first step (it names the
+// segment).
+struct Pos {
+  int b, kvh, qg, L, nb, seg, i, S;
 };
+
+// Steps per wave, computed identically by both kernels from the total step count T.
+__device__ __forceinline__ int steps_per_wave(int T, int W, int rmin) {
+  return max((T + W - 1) / W, rmin);
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint16_t* __restrict__ Qd, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int* __restrict__ seqlens, float* __restrict__ part_o,
-    float* __restrict__ part_lse, int B, int Hq, int Hkv, int Nk_max, int chunk, int max_chunks,
+    float* __restrict__ part_lse, int B, int Hq, int Hkv, int Nk_max, int rmin, int max_pieces,
     int QG, float c) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
   constexpr int VI = kStep * CH / 64;    // LDS-direct instructions per step
@@ -114,17 +125,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     }
   }
 
-  // ---- item list walk (items ordered batch-major, then chunk, K/V head, head group)
-  const int stride = gridDim.x * kWaves;
-  int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wave);
-  int cb = 0, cbase = 0;               // current batch and its first item index
+  // ---- work range of this wave
+  const int W = gridDim.x * kWaves;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wave);
+  const int per_b = Hkv * QG;  // segments per sequence
   // Sequence lengths are read with scalar loads (constant address space, uniform
   // index): they complete on their own counter, so reading one never waits for the
   // vector loads already in flight.
   const __attribute__((address_space(4))) int* sl =
       (const __attribute__((address_space(4))) int*)seqlens;
   // For up to 64 sequences the lengths are also kept one per lane, so a lookup is a
-  // register read instead of a memory round trip at every item change.
+  // register read instead of a memory round trip.
   const int sl_lane = (B <= 64 && lane < B) ? sl[lane] : 0;
   auto seqlen = [&](int bb) __attribute__((always_inline)) {
     const int ub = __builtin_amdgcn_readfirstlane(bb);
@@ -132,50 +143,65 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     L = L < 0 ? 0 : (L > Nk_max ? Nk_max : L);
     return __builtin_amdgcn_readfirstlane(L);
   };
-  auto locate = [&](int tt, Item& it) __attribute__((always_inline)) -> bool {
-    while (cb < B) {
-      const int n = ((seqlen(cb) + chunk - 1) / chunk) * per_batch_group;
-      if (tt < cbase + n) break;
-      cbase += n;
-      ++cb;
+  int T = 0;
+  for (int bb = 0; bb < B; ++bb) T += ((seqlen(bb) + kStep - 1) / kStep) * per_b;
+  T = __builtin_amdgcn_readfirstlane(T);
+  const int R = __builtin_amdgcn_readfirstlane(steps_per_wave(T, W, rmin));
+  const long long g_begin = (long long)w * R;
+  if (g_begin >= T) return;
+  const int g_end = (int)min((long long)T, g_begin + R);
+  int gs = (int)g_begin;  // global index of the current step
+
+  // Position of step i of segment seg of sequence bb (all arguments wave-uniform).
+  auto make_pos = [&](int bb, int L, int nb, int seg, int i, int S) __attribute__((always_inline)) {
+    Pos p;
+    p.b = __builtin_amdgcn_readfirstlane(bb);
+    p.L = __builtin_amdgcn_readfirstlane(L);
+    p.nb = __builtin_amdgcn_readfirstlane(nb);
+    p.seg = __builtin_amdgcn_readfirstlane(seg);
+    p.i = __builtin_amdgcn_readfirstlane(i);
+    p.S = __builtin_amdgcn_readfirstlane(S);
+    p.kvh = __builtin_amdgcn_readfirstlane(seg / QG);
+    p.qg = __builtin_amdgcn_readfirstlane(seg % QG);
+    return p;
+  };
+  // Position of global step g (0 <= g < T): skip whole sequences, then split the rest.
+  auto locate = [&](int g) __attribute__((always_inline)) {
+    int base = 0, bb = 0;
+    int nb = (seqlen(0) + kStep - 1) / kStep;
+    while (g >= base + nb * per_b) {
+      base += nb * per_b;
+      ++bb;
+      nb = (seqlen(bb) + kStep - 1) / kStep;
     }
-    if (cb >= B) return false;
-    const int L = seqlen(cb);
-    const int r = tt - cbase;
-    const int ci = r / per_batch_group;
-    const int rem = r % per_batch_group;
-    it.b = __builtin_amdgcn_readfirstlane(cb);
-    it.kvh = __builtin_amdgcn_readfirstlane(rem / QG);
-    it.qg = __builtin_amdgcn_readfirstlane(rem % QG);
-    it.c0 = __builtin_amdgcn_readfirstlane(ci * chunk);
-    it.c1 = __builtin_amdgcn_readfirstlane(min(ci * chunk + chunk, L));
-    return true;
+    const int r = g - base;
+    const int seg = r / nb;
+    return make_pos(bb, seqlen(bb), nb, seg, r % nb, base + seg * nb);
   };
 
-  Item cur, nxt;
-  if (!locate(t, cur)) return;
-  int cur_n0 = cur.c0;
+  Pos cur = locate(gs), nxt = cur;
 
   u32x4 kA[4][KS], kB[4][KS];  // two VGPR sets of K fragments
   bf16x8 qf[KS];
   f32x4 acc[DB];
   float m_run = kNegInf, l_run = 0.f, l_lse = 0.f;
 
-  // Buffer descriptors of one item's K or V slice, clipped after key c1 - 1.  Built
+  // Buffer descriptors of one sequence's K or V slice, clipped after key L - 1.  Built
   // from values forced into scalar registers so the loads need no per-lane loop.
-  auto rsrc_of = [&](const uint16_t* base, const Item& it) __attribute__((always_inline)) {
+  auto rsrc_of = [&](const uint16_t* base, const Pos& it) __attribute__((always_inline)) {
     const uint64_t a = reinterpret_cast<uint64_t>(base + ((size_t)it.b * Nk_max * Hkv + it.kvh) * D);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)(it.c1 - 1) * row_bytes + D * 2);
+    const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)(it.L - 1) * row_bytes + D * 2);
     return dmake_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nrec);
   };
-  // Issue the loads of the step at key n0 of item `it`: K into `kf`, V into LDS stage.
-  auto issue = [&](const Item& it, int n0, u32x4 (*kf)[KS], auto stage_c)
+  // Issue the loads of step `it`: K into `kf`, V into LDS stage.
+  auto issue = [&](const Pos& it, u32x4 (*kf)[KS], auto stage_c)
       __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_c)::value;
     const __amdgpu_buffer_rsrc_t rk = rsrc_of(Kc, it);
     const __amdgpu_buffer_rsrc_t rv = rsrc_of(Vc, it);
+    const int n0 = it.i * kStep;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -190,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
           (uint32_t)n0 * row_bytes + (uint32_t)(i & ~1) * (64 / CH) * row_bytes, 0, 0);
   };
 
-  auto item_begin = [&](const Item& it) __attribute__((always_inline)) {
+  auto item_begin = [&](const Pos& it) __attribute__((always_inline)) {
     const int hq0 = it.kvh * G + it.qg * 16;
     const int nq = min(16, G - it.qg * 16);
 #pragma unroll
@@ -206,7 +232,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     l_lse = 0.f;
   };
 
-  auto item_end = [&](const Item& it) __attribute__((always_inline)) {
+  // Partial result of the piece of segment `it` that this wave covered: record
+  // w - S / R of that segment (the pieces of a segment go to consecutive waves).
+  auto item_end = [&](const Pos& it) __attribute__((always_inline)) {
     float lr = l_run, le = l_lse;
     lr += __shfl_xor(lr, 16);
     lr += __shfl_xor(lr, 32);
@@ -216,21 +244,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int nq = min(16, G - it.qg * 16);
     if (l16 < nq) {
       const int hq = hq0 + l16;
-      const int ci = it.c0 / chunk;
+      const int pc = w - it.S / R;
       const float inv = 1.f / lr;
-      float* dst = part_o + (((size_t)it.b * Hq + hq) * max_chunks + ci) * D;
+      float* dst = part_o + (((size_t)it.b * Hq + hq) * max_pieces + pc) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = acc[db] * inv;
       if (g == 0)
-        part_lse[((size_t)it.b * Hq + hq) * max_chunks + ci] = (m_run + fast_log2(le)) * kLn2;
+        part_lse[((size_t)it.b * Hq + hq) * max_pieces + pc] = (m_run + fast_log2(le)) * kLn2;
     }
   };
 
   // One 64-key step: scores, online softmax, P V.
-  auto compute = [&](const Item& it, int n0, u32x4 (*kf)[KS], auto stage_c)
+  auto compute = [&](const Pos& it, u32x4 (*kf)[KS], auto stage_c)
       __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_c)::value;
+    const int n0 = it.i * kStep;
     f32x4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -241,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
                                                         qf[st], s[kb], 0, 0, 0);
     }
     float mx = kNegInf;
-    const int lim = it.c1 - 1 - (n0 + 4 * g);  // last valid key, relative to this lane's keys
+    const int lim = it.L - 1 - (n0 + 4 * g);  // last valid key, relative to this lane's keys
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -296,18 +325,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       }
   };
 
-  // Next step after (it, n0): the next 64 keys of the item, or the first step of the
-  // wave's next item.  Returns false when the wave has no more work.
-  auto advance = [&](const Item& it, int n0, Item& nit, int& nn0)
-      __attribute__((always_inline)) -> bool {
-    if (n0 + kStep < it.c1) {
-      nit = it;
-      nn0 = __builtin_amdgcn_readfirstlane(n0 + kStep);
-      return true;
+  // The step after `it` in this wave's range: the next step of the segment, or the
+  // first step of the next segment with keys.  Returns false at the end of the range.
+  auto advance = [&](const Pos& it, Pos& nt) __attribute__((always_inline)) -> bool {
+    if (gs + 1 >= g_end) return false;
+    gs = __builtin_amdgcn_readfirstlane(gs + 1);
+    int bb = it.b, L = it.L, nb = it.nb, seg = it.seg, i = it.i + 1, S = it.S;
+    if (i == nb) {
+      i = 0;
+      S += nb;
+      ++seg;
+      if (seg == per_b) {
+        // next sequence with at least one key (one exists: gs < g_end <= T)
+        seg = 0;
+        do {
+          ++bb;
+          L = seqlen(bb);
+        } while (L == 0);
+        nb = (L + kStep - 1) / kStep;
+      }
     }
-    t = __builtin_amdgcn_readfirstlane(t + stride);
-    if (!locate(t, nit)) return false;
-    nn0 = nit.c0;
+    nt = make_pos(bb, L, nb, seg, i, S);
     return true;
   };
 
@@ -315,30 +353,26 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   item_begin(cur);
-  issue(cur, cur_n0, kA, S0{});
+  issue(cur, kA, S0{});
   auto half = [&](u32x4 (*kc)[KS], u32x4 (*kn)[KS], auto stage_c, auto other_c)
       __attribute__((always_inline)) -> bool {
-    int nn0 = 0;
-    const bool more = advance(cur, cur_n0, nxt, nn0);
+    const bool more = advance(cur, nxt);
     if (more) {
-      issue(nxt, nn0, kn, other_c);
+      issue(nxt, kn, other_c);
       // wait for this step's loads: everything but the just-issued 4*KS + VI
       static_assert(4 * KS + VI == 32 || 4 * KS + VI == 16, "vmcnt encoding");
       if constexpr (4 * KS + VI == 32) __builtin_amdgcn_s_waitcnt(0x8f70);  // vmcnt(32)
       else __builtin_amdgcn_s_waitcnt(0x4f70);                             // vmcnt(16)
-      compute(cur, cur_n0, kc, stage_c);
+      compute(cur, kc, stage_c);
     } else {
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-      compute(cur, cur_n0, kc, stage_c);
+      compute(cur, kc, stage_c);
     }
-    const bool new_item = !more || nn0 == nxt.c0 && (nxt.b != cur.b || nxt.kvh != cur.kvh ||
-                                                      nxt.qg != cur.qg || nxt.c0 != cur.c0);
-    if (new_item) {
+    if (!more || nxt.S != cur.S) {
       item_end(cur);
       if (more) item_begin(nxt);
     }
     cur = nxt;
-    cur_n0 = nn0;
     return more;
   };
   while (true) {
@@ -347,48 +381,83 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   }
 }
 
-// Kernel 2: merge the chunks of one (query head, batch).  The four waves take every
-// fourth chunk; each lane owns D/64 columns.  Per wave: running maximum, weights and
-// weighted sums with several chunk rows in flight; the four partial results are then
-// combined through LDS with the same merge rule.
+// Kernel 2: merge the pieces of one (query head, batch).  The workgroup first finds
+// the segment's global start S and length n (sums over the sequence lengths, split
+// over the threads) and from them, with the split kernel's R, the number of pieces
+// (S + n - 1) / R - S / R + 1.  The four waves then take every fourth piece; each
+// lane owns D/64 columns.  Per wave: running maximum, weights and weighted sums with
+// several piece rows in flight; the four partial results are then combined through
+// LDS with the same merge rule.
 constexpr int kMergeThreads = 256;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const int* __restrict__ seqlens, const float* __restrict__ part_o,
-    const float* __restrict__ part_lse, float* __restrict__ O, float* __restrict__ LSE, int Hq,
-    int Nk_max, int chunk, int max_chunks) {
-  constexpr int W = kMergeThreads / 64;
+    const float* __restrict__ part_lse, float* __restrict__ O, float* __restrict__ LSE, int B,
+    int Hq, int Hkv, int QG, int Nk_max, int W, int rmin, int max_pieces) {
+  constexpr int NW = kMergeThreads / 64;
   constexpr int DPL = D / 64;  // columns per lane
-  __shared__ float s_m[W], s_l[W];
-  __shared__ float s_acc[W][D];
+  __shared__ float s_m[NW], s_l[NW];
+  __shared__ float s_acc[NW][D];
+  __shared__ int s_tot[NW], s_pre[NW];
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  int L = seqlens[b];
-  L = L < 0 ? 0 : (L > Nk_max ? Nk_max : L);
-  const int nc = (L + chunk - 1) / chunk;
+  const int per_b = Hkv * QG;
+  auto nsteps = [&](int bb) {
+    int L = seqlens[bb];
+    L = L < 0 ? 0 : (L > Nk_max ? Nk_max : L);
+    return (L + 63) / 64;
+  };
+  // T = all steps, pre = steps of the sequences before b
+  int tot = 0, pre = 0;
+  for (int bb = threadIdx.x; bb < B; bb += kMergeThreads) {
+    const int n = nsteps(bb) * per_b;
+    tot += n;
+    pre += (bb < b) ? n : 0;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    tot += __shfl_xor(tot, off);
+    pre += __shfl_xor(pre, off);
+  }
+  if (lane == 0) {
+    s_tot[wave] = tot;
+    s_pre[wave] = pre;
+  }
+  __syncthreads();
+  int T = 0, base = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    T += s_tot[i];
+    base += s_pre[i];
+  }
+  const int R = steps_per_wave(T, W, rmin);
+  const int G = Hq / Hkv;
+  const int nb = nsteps(b);
+  const int seg = (hq / G) * QG + (hq % G) / 16;
+  const int S = base + seg * nb;
+  const int nc = nb > 0 ? (S + nb - 1) / R - S / R + 1 : 0;
   const size_t row = (size_t)b * Hq + hq;
-  const float* pl = part_lse + row * max_chunks;
-  const float* po = part_o + row * max_chunks * D + lane * DPL;
+  const float* pl = part_lse + row * max_pieces;
+  const float* po = part_o + row * max_pieces * D + lane * DPL;
 
-  // Wave-level maximum over this wave's chunks (every lane reads the same lse values).
+  // Wave-level maximum over this wave's pieces (every lane reads the same lse values).
   float M = kNegInf;
-  for (int ci = wave; ci < nc; ci += W) M = fmaxf(M, pl[ci]);
+  for (int ci = wave; ci < nc; ci += NW) M = fmaxf(M, pl[ci]);
   float ssum = 0.f;
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   const float Mref = (M == kNegInf) ? 0.f : M;
   int ci = wave;
-  for (; ci + 3 * W < nc; ci += 4 * W) {  // four chunk rows in flight
+  for (; ci + 3 * NW < nc; ci += 4 * NW) {  // four piece rows in flight
     float lv[4], ov[4][DPL];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      lv[u] = pl[ci + u * W];
+      lv[u] = pl[ci + u * NW];
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) ov[u][i] = po[(size_t)(ci + u * W) * D + i];
+      for (int i = 0; i < DPL; ++i) ov[u][i] = po[(size_t)(ci + u * NW) * D + i];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -398,7 +467,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
       for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, ov[u][i], acc[i]);
     }
   }
-  for (; ci < nc; ci += W) {
+  for (; ci < nc; ci += NW) {
     const float w = fast_exp2((pl[ci] - Mref) * kLog2e);
     ssum += w;
 #pragma unroll
@@ -412,21 +481,21 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   for (int i = 0; i < DPL; ++i) s_acc[wave][lane * DPL + i] = acc[i];
   __syncthreads();
 
-  // Combine the four waves (a wave that had no chunk contributes weight 0).
+  // Combine the four waves (a wave that had no piece contributes weight 0).
   float Mt = kNegInf;
 #pragma unroll
-  for (int w = 0; w < W; ++w) Mt = fmaxf(Mt, s_m[w]);
+  for (int w = 0; w < NW; ++w) Mt = fmaxf(Mt, s_m[w]);
   const float Mtr = (Mt == kNegInf) ? 0.f : Mt;
-  float wsc[W], St = 0.f;
+  float wsc[NW], St = 0.f;
 #pragma unroll
-  for (int w = 0; w < W; ++w) {
+  for (int w = 0; w < NW; ++w) {
     wsc[w] = (s_m[w] == kNegInf) ? 0.f : fast_exp2((s_m[w] - Mtr) * kLog2e);
     St += wsc[w] * s_l[w];
   }
   for (int d = threadIdx.x; d < D; d += kMergeThreads) {
     float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) o = fmaf(wsc[w], s_acc[w][d], o);
+    for (int w = 0; w < NW; ++w) o = fmaf(wsc[w], s_acc[w][d], o);
     O[row * D + d] = (nc > 0) ? o / St : 0.f;
   }
   if (threadIdx.x == 0) LSE[row] = (nc > 0) ? Mtr + fast_log2(St) * kLn2 : kNegInf;
@@ -443,15 +512,16 @@ hipError_t launch(const DecodeArgs& a, hipStream_t s) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
       cus = v;
   }
+  const int rmin = a.chunk / kStep;  // a piece has at least `chunk` keys' worth of steps
   hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)cus), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.seqlens, a.part_o, a.part_lse, a.B,
-                     a.Hq, a.Hkv, a.Nk_max, a.chunk, a.max_chunks, QG, a.scale * kLog2e);
+                     a.Hq, a.Hkv, a.Nk_max, rmin, a.max_pieces, QG, a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.Hq, (unsigned)a.B),
                      dim3(kMergeThreads), 0, s, a.seqlens, a.part_o, a.part_lse, a.o, a.lse,
-                     a.Hq, a.Nk_max, a.chunk, a.max_chunks);
+                     a.B, a.Hq, a.Hkv, QG, a.Nk_max, cus * kWaves, rmin, a.max_pieces);
   return hipGetLastError();
 }
 

@@ -21,8 +21,9 @@ struct PrefillArgs {
 };
 
 // Split-KV decode: q [B,Hq,d], caches [B,Nk_max,Hkv,d], seqlens [B] (device),
-// O [B,Hq,d] fp32, LSE [B,Hq] fp32, workspace = partial O [B,Hq,C,d] fp32 followed by
-// partial LSE [B,Hq,C] fp32 with C = ceil(Nk_max / chunk).
+// O [B,Hq,d] fp32, LSE [B,Hq] fp32, workspace = partial O [B,Hq,P,d] fp32 followed by
+// partial LSE [B,Hq,P] fp32 with P = max_pieces = ceil(ceil(Nk_max / 64) / (chunk / 64)) + 1,
+// the most pieces one (batch, K/V head) can be cut into.
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -32,7 +33,7 @@ struct DecodeArgs {
   float* lse;
   float* part_o;
   float* part_lse;
-  int B, Hq, Hkv, Nk_max, d, chunk, max_chunks;
+  int B, Hq, Hkv, Nk_max, d, chunk, max_pieces;
   float scale;
 };
 
@@ -41,12 +42,12 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t s);
 
 // Workspace split used by both the size query and the launcher.
-inline size_t decode_part_o_bytes(int B, int Hq, int max_chunks, int d) {
-  size_t n = (size_t)B * Hq * max_chunks * d * sizeof(float);
+inline size_t decode_part_o_bytes(int B, int Hq, int max_pieces, int d) {
+  size_t n = (size_t)B * Hq * max_pieces * d * sizeof(float);
   return (n + 255) & ~(size_t)255;
 }
-inline size_t decode_part_lse_bytes(int B, int Hq, int max_chunks) {
-  size_t n = (size_t)B * Hq * max_chunks * sizeof(float);
+inline size_t decode_part_lse_bytes(int B, int Hq, int max_pieces) {
+  size_t n = (size_t)B * Hq * max_pieces * sizeof(float);
   return (n + 255) & ~(size_t)255;
 }
 

@@ -81,9 +81,11 @@ def test_forward_rejects(L, entry, kw, status):
 
 def test_workspace_bytes(L):
     n = fa.fa_decode_splitkv_workspace_bytes(16, 64, 32768, 128, 256)
-    chunks = 32768 // 256
-    want_o = 16 * 64 * chunks * 128 * 4
-    want_l = 16 * 64 * chunks * 4
+    # a (batch, K/V head) of 512 steps of 64 keys, split in runs of at least 4 steps
+    # that may start or end inside it: at most 128 + 1 pieces
+    pieces = 32768 // 256 + 1
+    want_o = 16 * 64 * pieces * 128 * 4
+    want_l = 16 * 64 * pieces * 4
     assert n == ((want_o + 255) // 256) * 256 + ((want_l + 255) // 256) * 256
     assert fa.fa_decode_splitkv_workspace_bytes(1, 1, 1, 64, 64) > 0
     for bad in [(0, 1, 1, 64, 256), (1, 1, 0, 64, 256), (1, 1, 1, 80, 256), (1, 1, 1, 64, 100),

@@ -187,6 +187,11 @@ DEC = [  # B, Hq, Hkv, d, Nk_max, lengths, chunk
     (2, 8, 8, 64, 700, [1, 700], 64),
     (2, 32, 1, 128, 2048, [2048, 1000], 512),   # 32 heads per K/V head: two head groups
     (2, 4, 2, 64, 300, [300, 63], 128),
+    (3, 8, 2, 128, 3000, [2000, 3000, 1500], 1024),  # pieces of at least 16 steps
+    # many short sequences: one wave's run of steps crosses several (batch, head) segments
+    (40, 8, 2, 64, 200, [1 + (37 * i) % 200 for i in range(40)], 64),
+    # more than 64 sequences (lengths read from memory, not kept one per lane)
+    (70, 4, 1, 64, 130, [1 + (53 * i) % 130 for i in range(70)], 64),
 ]
 
 
@@ -204,6 +209,29 @@ def test_decode_edges(case):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.decode_attention(q, kc, vc, lengths, scale)
     _cmp(o.cpu(), lse.cpu(), o_ref, lse_ref, TOL_BF16, f"decode {case}")
+
+
+def test_decode_empty_sequences():
+    """A sequence with no cached key gets O = 0 and LSE = -inf (the header's documented
+    clamp); the work of the other sequences is unaffected."""
+    lens = [0, 300, 0, 1, 0]
+    B, Hq, Hkv, d, Nk_max = len(lens), 8, 2, 128, 512
+    lengths = torch.tensor(lens, dtype=torch.int32)
+    lengths, q, kc, vc = W.decode_inputs(B, Hq, Hkv, d, Nk_max, 0, 0, seed=12, lengths=lengths)
+    dev = _dev()
+    o = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev)
+    scale = 1 / math.sqrt(d)
+    fa.fa_decode_splitkv(q.to(dev), kc.to(dev), vc.to(dev), lengths.to(dev), scale=scale,
+                         chunk=64, o=o, lse=lse)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    live = [b for b, L in enumerate(lens) if L > 0]
+    o_ref, lse_ref = oracle.decode_attention(q, kc, vc, lengths, scale, batches=live)
+    _cmp(o[live], lse[live], o_ref[live], lse_ref[live], TOL_BF16, "decode live rows")
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(o[b] == 0) and torch.all(lse[b] == float("-inf")), b
 
 
 # ---------------------------------------------------------------------------
