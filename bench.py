@@ -4,8 +4,9 @@ One step = one pass of the whole hot path on resident synthetic inputs:
   * prefill: fa_forward on the causal GQA long-context workload
     (bf16, B=1, Hq=64, Hkv=8, N=32768, d=128) — one kernel launch;
   * decode:  fa_decode_splitkv on the GQA decode workload (bf16, B=16, Hq=64,
-    Hkv=8, d=128, per-sequence key counts ~U[4096, 32768], 256-key chunks) —
-    the split kernel and the merge kernel.
+    Hkv=8, d=128, per-sequence key counts ~U[4096, 32768], chunk=256: key work
+    split over the waves in runs of at least 256 keys) — the split kernel and
+    the merge kernel.
 `value` is the prefill's algorithmic TFLOP/s (4*B*Hq*Nq*Nk*d / 2 for causal) over
 its measured kernel time; the decode's HBM GB/s (compulsory K/V/q/O/LSE bytes)
 is reported alongside.  Kernel times come from HIP events recorded on the
@@ -82,32 +83,37 @@ def copy_calib():
 
 def cpu_baseline_prefill(cfg, target_s):
     """The fp64 oracle on a bounded sample of the prefill workload: the last R query
-    rows of query head 0 (each sees ~all keys), R grown until ~target_s."""
+    rows (each sees ~all keys) of the first H query heads, R grown to the whole
+    sequence first, then H, until the sample takes ~target_s."""
     import torch
     import oracle
     import workloads as W
     q, k, v = W.prefill_inputs_for(cfg)
     N, d = cfg.Nq, cfg.d
-    R = 64
-    t_used = 0.0
+    R, H = 64, 1
     while True:
         r0 = N - R
         t0 = time.perf_counter()
-        oracle.attention(q, k, v, cfg.scale, cfg.causal, heads=[0], rows=(r0, N), row_block=256)
+        oracle.attention(q, k, v, cfg.scale, cfg.causal, heads=list(range(H)), rows=(r0, N),
+                         row_block=256)
         dt = time.perf_counter() - t0
-        if dt * 2 > target_s or R >= N:
+        if dt * 2 > target_s or (R >= N and H >= cfg.Hq):
             break
-        t_used += dt
-        R = min(N, R * 2)
+        if R < N:
+            R = min(N, R * 2)
+        else:
+            H = min(cfg.Hq, H * 2)
     if cfg.causal:
         keys = sum(min(cfg.Nk, i + (cfg.Nk - cfg.Nq) + 1) for i in range(r0, N))
     else:
         keys = R * cfg.Nk
+    keys *= H
     flops = 4.0 * d * keys
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{cfg.name}: query head 0, query rows {r0}..{N - 1} ({R} rows, "
-                      f"{keys} visible (row,key) pairs), fp64 torch CPU standard attention"}
+            "sample": f"{cfg.name}: query heads 0..{H - 1}, query rows {r0}..{N - 1} ({R} rows "
+                      f"per head, {keys} visible (row,key) pairs), fp64 torch CPU standard "
+                      f"attention"}
 
 
 def cpu_baseline_decode(cfg, lengths, q, kc, vc, target_s):
@@ -249,6 +255,9 @@ def main():
                             "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "avg_call_ms": round(avg_dec, 4),
                             "kernels": "split + merge (one call)",
+                            "split": "key work of all (batch, K/V head) segments cut into equal "
+                                     "per-wave runs of 64-key steps, pieces of >= chunk keys; "
+                                     "LSE merge of the pieces",
                             "bytes_per_call": dbytes,
                             "sum_seqlens": int(dec["lengths"].sum().item()),
                             "traffic_split": profiled_traffic("decode_split_kernel<128>"),

@@ -45,6 +45,7 @@ namespace {
 constexpr int kThreads = 256;  // four independent wave workers per workgroup
 constexpr int kWaves = 4;
 constexpr int kStep = 64;      // keys per step
+constexpr int kNT = 2;         // cache policy of the K/V loads: non-temporal
 
 typedef __attribute__((address_space(3))) void dlds_void_t;
 typedef __bf16 dbf16x4 __attribute__((ext_vector_type(4)));
@@ -195,7 +196,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)(it.L - 1) * row_bytes + D * 2);
     return dmake_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nrec);
   };
-  // Issue the loads of step `it`: K into `kf`, V into LDS stage.
+  // Issue the loads of step `it`: K into `kf`, V into LDS stage.  Every cache byte is
+  // read once, so the loads are marked non-temporal.
   auto issue = [&](const Pos& it, u32x4 (*kf)[KS], auto stage_c)
       __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_c)::value;
@@ -207,13 +209,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
       for (int st = 0; st < KS; ++st)
         kf[kb][st] = __builtin_amdgcn_raw_buffer_load_b128(
-            rk, k_lane + 64u * st, (uint32_t)(n0 + 16 * kb) * row_bytes, 0);
+            rk, k_lane + 64u * st, (uint32_t)(n0 + 16 * kb) * row_bytes, kNT);
     uint16_t* dst = stage == 1 ? vst1[wave] : vst0[wave];
 #pragma unroll
     for (int i = 0; i < VI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rv, (dlds_void_t*)(dst + i * 512), 16, v_lane[i & 1],
-          (uint32_t)n0 * row_bytes + (uint32_t)(i & ~1) * (64 / CH) * row_bytes, 0, 0);
+          (uint32_t)n0 * row_bytes + (uint32_t)(i & ~1) * (64 / CH) * row_bytes, 0, kNT);
   };
 
   auto item_begin = [&](const Pos& it) __attribute__((always_inline)) {
