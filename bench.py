@@ -243,6 +243,7 @@ def main():
                                  if pcfg.d == 128 and pcfg.causal else None),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "avg_launch_ms": round(avg_pre, 4),
+                     "median_launch_ms": round(sorted(pre_ms)[K // 2], 4),
                      "flop_per_launch": flops},
         "wall_s_timed_region": round(wall, 3),
     }
@@ -254,6 +255,7 @@ def main():
         result["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
                             "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "avg_call_ms": round(avg_dec, 4),
+                            "median_call_ms": round(sorted(dec_ms)[K // 2], 4),
                             "kernels": "split + merge (one call)",
                             "split": "key work of all (batch, K/V head) segments cut into equal "
                                      "per-wave runs of 64-key steps, pieces of >= chunk keys; "
