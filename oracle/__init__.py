@@ -23,6 +23,7 @@ from .attention import (  # noqa: F401
     attention,
     attention_probs,
     decode_attention,
+    decode_attention_paged,
     lse_merge,
     online_softmax_update,
     online_attention_rows,

@@ -152,6 +152,43 @@ def decode_attention(q, k_cache, v_cache, lengths, scale: float,
     return o, lse
 
 
+def decode_attention_paged(q, k_pages, v_pages, block_table, lengths, page_size: int,
+                           scale: float, heads: Optional[Sequence[int]] = None,
+                           batches: Optional[Iterable[int]] = None):
+    """One decode step over a paged KV cache.
+
+    [LLM-basics] §8 (PagedAttention): the cache is kept in fixed-size physical
+    blocks ("pages") and a per-sequence block table maps the sequence's logical
+    block j -- its keys j*page_size .. (j+1)*page_size - 1 -- to a physical page;
+    several sequences may point at the same page.  k_pages and v_pages are
+    [num_pages, page_size, Hkv, d]; block_table is [B, max_pages].  The step is
+    the decode attention of [LLM-basics] ②-3 / ②-4 over the first lengths[b]
+    logical keys, gathered page by page through the table (rows of the last page
+    at or beyond the length are never read).  Returns O [B, Hq, d] and LSE [B, Hq]
+    in float64 (NaN where a head or batch was not requested).
+    """
+    q = _as64(q)
+    B, Hq, d = q.shape
+    o = torch.full((B, Hq, d), float("nan"), dtype=f64)
+    lse = torch.full((B, Hq), float("nan"), dtype=f64)
+    hs = list(heads) if heads is not None else list(range(Hq))
+    for b in (batches if batches is not None else range(B)):
+        L = int(lengths[b])
+        rows_k, rows_v = [], []
+        for j in range((L + page_size - 1) // page_size):
+            page = int(block_table[b][j])
+            n = min(page_size, L - j * page_size)
+            rows_k.append(_as64(k_pages[page, :n]))
+            rows_v.append(_as64(v_pages[page, :n]))
+        kk = torch.cat(rows_k, dim=0)  # [L, Hkv, d]
+        vv = torch.cat(rows_v, dim=0)
+        oo, ll = attention(q[b].reshape(1, 1, Hq, d), kk.unsqueeze(0), vv.unsqueeze(0), scale,
+                           causal=False, heads=hs)
+        o[b, hs] = oo[0, 0, hs]
+        lse[b, hs] = ll[0, hs, 0]
+    return o, lse
+
+
 def online_softmax_update(m_prev: torch.Tensor, l_prev: torch.Tensor, acc_prev: torch.Tensor,
                           s_block: torch.Tensor, v_block: torch.Tensor):
     """One block step of the online softmax, per row.

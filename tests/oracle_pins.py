@@ -345,6 +345,70 @@ def pin_decode_matches_prefill(orc):
     _close(o[0], vc[0, 0].repeat_interleave(Hq // Hkv, dim=0), 0.0, "L=1 decode")
 
 
+def _paged_pool(num_pages, page_size, Hkv, d):
+    kp = torch.full((num_pages, page_size, Hkv, d), float("nan"), dtype=f64)
+    vp = torch.full((num_pages, page_size, Hkv, d), float("nan"), dtype=f64)
+    return kp, vp
+
+
+def pin_paged_constant_pages(orc):
+    """[LLM-basics] §8: logical block j of a sequence lives in the physical page its
+    block table names.  With K = 0 every valid key has score 0, so each query head's
+    output is the plain mean of the valid V rows and LSE = ln L.  Every physical page
+    holds one constant V row value, so the mean is the page constants weighted by how
+    many of the sequence's keys fall in each page (the last page partly).  Tables are
+    permuted, two sequences share a page, rows past the length and unused pages are NaN."""
+    page_size, Hkv, d, Hq = 4, 2, 3, 4
+    num_pages = 7
+    kp, vp = _paged_pool(num_pages, page_size, Hkv, d)
+    const = {p: torch.tensor([[p + 1.0, -2.0 * p, 0.5 * p * p], [3.0 - p, p / 4.0, 1.0]],
+                             dtype=f64) for p in range(num_pages)}
+    table = [[5, 2, 0, -1], [2, 6, -1, -1], [3, -1, -1, -1]]
+    lengths = [10, 5, 1]
+    for b, L in enumerate(lengths):
+        for j in range((L + page_size - 1) // page_size):
+            page = table[b][j]
+            n = min(page_size, L - j * page_size)
+            kp[page, :n] = 0.0
+            vp[page, :n] = const[page].unsqueeze(0).expand(n, Hkv, d)
+    q = _rand((3, Hq, d), 130)
+    o, lse = orc.decode_attention_paged(q, kp, vp, table, lengths, page_size, 0.7)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    G = Hq // Hkv
+    for b, L in enumerate(lengths):
+        want = torch.zeros((Hkv, d), dtype=f64)
+        for j in range((L + page_size - 1) // page_size):
+            n = min(page_size, L - j * page_size)
+            want += n * const[table[b][j]]
+        want /= L
+        for h in range(Hq):
+            _close(o[b, h], want[h // G], 1e-14, f"paged mean b={b} h={h}")
+            _close(lse[b, h:h + 1], [math.log(L)], 1e-14, f"paged LSE b={b}")
+
+
+def pin_paged_dominant_key(orc):
+    """One logical key position t gets a score 60 above every other key, so O is that key's
+    V row (to ~1e-26): checks that logical position t is read from row t mod page_size of
+    page table[t div page_size], for t at the first and last row of a page and inside the
+    partial last page."""
+    page_size, Hkv, d, Hq = 4, 1, 2, 2
+    table = [[3, 0, 4]]
+    L = 11
+    for t in (0, 3, 4, 7, 8, 10):
+        kp, vp = _paged_pool(5, page_size, Hkv, d)
+        for j in range(3):
+            n = min(page_size, L - j * page_size)
+            kp[table[0][j], :n] = 0.0
+            vp[table[0][j], :n] = _rand((n, Hkv, d), 140 + 10 * t + j)
+        page, row = table[0][t // page_size], t % page_size
+        kp[page, row] = 100.0
+        q = torch.full((1, Hq, d), 0.3, dtype=f64)       # score(t) = 0.3 * 100 * d * scale = 60
+        o, lse = orc.decode_attention_paged(q, kp, vp, table, [L], page_size, 1.0)
+        for h in range(Hq):
+            _close(o[0, h], vp[page, row, 0], 1e-20, f"dominant paged key t={t}")
+            _close(lse[0, h:h + 1], [60.0 + 0.0], 1e-12, f"dominant paged LSE t={t}")
+
+
 # ---------------------------------------------------------------------------
 # independent re-computations
 # ---------------------------------------------------------------------------
@@ -408,6 +472,8 @@ def pin_sdpa_crosscheck(orc):
 
 
 ALL_PINS = [
+    pin_paged_constant_pages,
+    pin_paged_dominant_key,
     pin_worked_example_printed,
     pin_worked_example_closed_form,
     pin_softmax_examples,

@@ -36,8 +36,15 @@ MUTANTS = {
     "merge weight vs M": ("wn = torch.exp(lse_parts - lse)", "wn = torch.exp(lse_parts - M)"),
     "final O not normalised": ("return acc / l.unsqueeze(-1), m + torch.log(l)",
                                "return acc, m + torch.log(l)"),
-    "decode reads one row short": ("L = int(lengths[b])", "L = max(int(lengths[b]) - 1, 1)"),
+    "decode reads one row short": ("L = int(lengths[b])\n        kk = _as64(k_cache[b, :L])",
+                                   "L = max(int(lengths[b]) - 1, 1)\n        kk = _as64(k_cache[b, :L])"),
     "decode reads past length": ("kk = _as64(k_cache[b, :L])", "kk = _as64(k_cache[b, :L + 1])"),
+    "paged ignores block table": ("page = int(block_table[b][j])", "page = j"),
+    "paged reads whole last page": ("n = min(page_size, L - j * page_size)", "n = page_size"),
+    "paged misses partial last page": ("for j in range((L + page_size - 1) // page_size):",
+                                       "for j in range(L // page_size):"),
+    "paged takes the next table entry": ("page = int(block_table[b][j])",
+                                         "page = int(block_table[b][j + 1])"),
 }
 
 

@@ -158,3 +158,37 @@ def decode_bytes(lengths, Hq: int, Hkv: int, d: int) -> float:
     B = len(lengths)
     kv = 2.0 * total_keys * Hkv * d * 2
     return kv + B * Hq * d * 2 + B * Hq * d * 4 + B * Hq * 4
+
+
+def paged_from_contiguous(k_cache: torch.Tensor, v_cache: torch.Tensor, lengths, page_size: int,
+                          seed: int = 0, spare_pages: int = 0, nan_pad: bool = True):
+    """Scatter a contiguous cache [B, Nk_max, Hkv, d] into a page pool.
+
+    Returns (k_pages, v_pages [num_pages, page_size, Hkv, d], block_table int32
+    [B, ceil(Nk_max / page_size)]).  Sequence b's logical page j goes to a
+    physical page drawn from a seeded permutation of the pool (so the table is
+    not the identity); `spare_pages` unused pages are added to the pool.  Rows
+    of a page past the sequence's length, and the spare pages, are NaN when
+    ``nan_pad`` is set; table entries past a sequence's last page are -1.
+    """
+    B, Nk_max, Hkv, d = k_cache.shape
+    maxp = (Nk_max + page_size - 1) // page_size
+    npg = [(int(L) + page_size - 1) // page_size for L in lengths]
+    num_pages = sum(npg) + spare_pages
+    g = torch.Generator("cpu").manual_seed(seed)
+    perm = torch.randperm(max(num_pages, 1), generator=g).tolist()
+    fill = float("nan") if nan_pad else 0.0
+    kp = torch.full((max(num_pages, 1), page_size, Hkv, d), fill, dtype=k_cache.dtype)
+    vp = torch.full((max(num_pages, 1), page_size, Hkv, d), fill, dtype=v_cache.dtype)
+    table = torch.full((B, maxp), -1, dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        L = int(lengths[b])
+        for j in range(npg[b]):
+            page = perm[nxt]
+            nxt += 1
+            n = min(page_size, L - j * page_size)
+            kp[page, :n] = k_cache[b, j * page_size:j * page_size + n]
+            vp[page, :n] = v_cache[b, j * page_size:j * page_size + n]
+            table[b, j] = page
+    return kp, vp, table
