@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--prefill", default="c4", choices=["c2", "c3", "c4"],
                     help="prefill workload (default: the long-context GQA one)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-KV decode measurement (reported beside the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -114,6 +116,44 @@ def cpu_baseline_prefill(cfg, target_s):
             "sample": f"{cfg.name}: query heads 0..{H - 1}, query rows {r0}..{N - 1} ({R} rows "
                       f"per head, {keys} visible (row,key) pairs), fp64 torch CPU standard "
                       f"attention"}
+
+
+def bench_paged(fa, W, dcfg, dec, dev, K, page_size=256):
+    """The same decode step with the KV cache scattered over a permuted pool of
+    `page_size`-key pages (paged KV cache), timed on its own after the step."""
+    import torch
+    print("[bench] paged decode", file=sys.stderr, flush=True)
+    kp, vp, table = W.paged_from_contiguous(dec["kc"], dec["vc"], dec["lengths"], page_size,
+                                            seed=7, spare_pages=9)
+    kp, vp, table = kp.to(dev), vp.to(dev), table.to(dev)
+    o = torch.empty_like(dec["o"])
+    lse = torch.empty_like(dec["lse"])
+    nbytes = fa.fa_decode_splitkv_workspace_bytes(dcfg.B, dcfg.Hq, table.shape[1] * page_size,
+                                                  dcfg.d, dcfg.chunk)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+
+    def call():
+        fa.fa_decode_paged(dec["dq"], kp, vp, table, dec["dl"], scale=dcfg.scale,
+                           chunk=dcfg.chunk, o=o, lse=lse, workspace=ws)
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / K
+    dbytes = W.decode_bytes(dec["lengths"].tolist(), dcfg.Hq, dcfg.Hkv, dcfg.d)
+    gbs = dbytes / (avg * 1e-3) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "bound": "hbm", "peak": PEAK_HBM_GBS,
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_call_ms": round(avg, 4),
+            "median_call_ms": round(sorted(ms)[K // 2], 4), "page_size": page_size,
+            "pool_pages": int(kp.shape[0]),
+            "layout": "c5 keys in a seeded permutation of a page pool, block table per sequence"}
 
 
 def cpu_baseline_decode(cfg, lengths, q, kc, vc, target_s):
@@ -264,6 +304,8 @@ def main():
                             "sum_seqlens": int(dec["lengths"].sum().item()),
                             "traffic_split": profiled_traffic("decode_split_kernel<128>"),
                             "traffic_merge": profiled_traffic("decode_merge_kernel<128>")}
+    if dec and not args.no_paged:
+        result["decode_paged"] = bench_paged(fa, W, dcfg, dec, dev, K)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_prefill(pcfg, args.cpu_seconds)

@@ -61,7 +61,8 @@ typedef enum {
   FA_ERR_NULL = -1,        /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,       /* B, H, N or d <= 0; Hq % Hkv != 0; causal with Nq > Nk;
                               sizes whose element counts overflow 32-bit row indexing */
-  FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}; decode chunk not a positive multiple of 64 */
+  FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}; decode chunk or page size not a positive
+                              multiple of 64 */
   FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = -5,   /* decode workspace missing or smaller than required */
   FA_ERR_HIP = -6          /* the kernel launch failed (hipGetLastError) */
@@ -145,6 +146,36 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       const int* seqlens_k, float* o, float* lse,
                       int B, int Hq, int Hkv, int Nk_max, int d, float scale, int chunk,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_decode_paged — fa_decode_splitkv over a paged KV cache.
+ *
+ * [LLM-basics] §8 (PagedAttention): the cache is a pool of fixed-size pages and each
+ * sequence has a block table that maps its logical page j (keys j*page_size ..
+ * (j+1)*page_size - 1) to a physical page; sequences may share pages.  The step, the
+ * work split and the merge are those of fa_decode_splitkv, with every 64-key step
+ * read from the page the table names.
+ *
+ *   q            bf16  [B, Hq, d]                          (read)
+ *   k_pages      bf16  [num_pages, page_size, Hkv, d]      (read; only rows of the pages
+ *   v_pages      bf16  [num_pages, page_size, Hkv, d]       a sequence uses, below its length)
+ *   block_table  int32 [B, max_pages] on the device; entries 0 <= e < num_pages for the
+ *                ceil(seqlens_k[b] / page_size) pages in use (later entries are never
+ *                read); the kernel clamps entries into [0, num_pages) for memory safety
+ *   seqlens_k    int32 [B] on the device, 1 <= seqlens_k[b] <= max_pages * page_size
+ *                (clamped as in fa_decode_splitkv; 0 keys gives O = 0, LSE = -inf)
+ *   o, lse       fp32 [B, Hq, d], [B, Hq]                  (written)
+ *   page_size    keys per page, a positive multiple of 64
+ *   chunk        as in fa_decode_splitkv
+ *   workspace    at least fa_decode_splitkv_workspace_bytes(B, Hq, max_pages * page_size,
+ *                d, chunk) bytes, 16-byte aligned
+ * block_table needs 4-byte alignment.  Returns FA_OK or a negative fa_status.
+ */
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                    const int* block_table, const int* seqlens_k, float* o, float* lse,
+                    int B, int Hq, int Hkv, int num_pages, int page_size, int max_pages, int d,
+                    float scale, int chunk, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
 
 /* fa_status_str — a static, human-readable string for a status code. */
 const char* fa_status_str(int status);

@@ -12,6 +12,8 @@ Functions (same names as the C entry points):
   fa_decode_splitkv_workspace_bytes(B, Hq, Nk_max, d, chunk=256)
   fa_decode_splitkv(q, k_cache, v_cache, seqlens_k, scale=None, chunk=256, o=None,
                     lse=None, workspace=None, stream=None)
+  fa_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, scale=None, chunk=256,
+                  o=None, lse=None, workspace=None, stream=None)
   fa_status_str(status)
 """
 from __future__ import annotations
@@ -59,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_splitkv_workspace_bytes.restype = sz
     L.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     L.fa_decode_splitkv.restype = i
+    L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.fa_decode_paged.restype = i
     L.fa_status_str.argtypes = [i]
     L.fa_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -166,4 +170,38 @@ def fa_decode_splitkv(q, k_cache, v_cache, seqlens_k, scale: Optional[float] = N
                                  _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_decode_splitkv")
+    return o, lse
+
+
+def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, scale: Optional[float] = None,
+                    chunk: int = 256, o=None, lse=None, workspace=None, stream=None):
+    """q bf16 [B,Hq,d]; page pools bf16 [num_pages,page_size,Hkv,d]; block_table int32
+    [B,max_pages] and seqlens_k int32 [B] on the GPU -> (O fp32 [B,Hq,d], LSE fp32 [B,Hq])."""
+    import torch
+    _check_tensor(q, "q", torch.bfloat16, 3)
+    _check_tensor(k_pages, "k_pages", torch.bfloat16, 4)
+    _check_tensor(v_pages, "v_pages", torch.bfloat16, 4)
+    _check_tensor(block_table, "block_table", torch.int32, 2)
+    _check_tensor(seqlens_k, "seqlens_k", torch.int32, 1)
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, dc = k_pages.shape
+    max_pages = block_table.shape[1]
+    if (tuple(v_pages.shape) != tuple(k_pages.shape) or dc != d or seqlens_k.shape[0] != B
+            or block_table.shape[0] != B):
+        raise ValueError("paged decode shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = fa_decode_splitkv_workspace_bytes(B, Hq, max_pages * page_size, d, chunk)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                               _ptr(seqlens_k), _ptr(o), _ptr(lse), B, Hq, Hkv, num_pages,
+                               page_size, max_pages, d, float(scale), int(chunk), _ptr(workspace),
+                               int(workspace.numel() * workspace.element_size()), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_paged")
     return o, lse

@@ -103,6 +103,41 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   return fa::launch_decode_splitkv(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                    const int* block_table, const int* seqlens_k, float* o, float* lse, int B,
+                    int Hq, int Hkv, int num_pages, int page_size, int max_pages, int d,
+                    float scale, int chunk, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seqlens_k || !o || !lse) return FA_ERR_NULL;
+  if (num_pages <= 0 || page_size <= 0 || max_pages <= 0) return FA_ERR_SHAPE;
+  if (page_size % 64 != 0) return FA_ERR_UNSUPPORTED;
+  if ((long long)max_pages * page_size > INT_MAX) return FA_ERR_SHAPE;
+  const int Nk_max = max_pages * page_size;
+  const int st = check_decode_sizes(B, Hq, Hkv, Nk_max, d, chunk);
+  if (st != FA_OK) return st;
+  // one page of one K/V head is addressed with 32-bit offsets; the page index with 64
+  if ((long long)page_size * Hkv * d * 2 > INT_MAX || (long long)B * max_pages > INT_MAX)
+    return FA_ERR_SHAPE;
+  if (misaligned(q) || misaligned(k_pages) || misaligned(v_pages) || misaligned(o) ||
+      (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return FA_ERR_ALIGN;
+  const int mp = max_pieces_of(Nk_max, chunk);
+  const size_t need = fa::decode_part_o_bytes(B, Hq, mp, d) + fa::decode_part_lse_bytes(B, Hq, mp);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return FA_ERR_ALIGN;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             fa::decode_part_o_bytes(B, Hq, mp, d));
+  fa::DecodeArgs a{q, k_pages, v_pages, seqlens_k, o, lse, part_o, part_lse,
+                   B, Hq, Hkv, Nk_max, d, chunk, mp, scale};
+  a.block_table = block_table;
+  a.page_size = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  return fa::launch_decode_splitkv(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
@@ -110,7 +145,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (non-positive, Hq % Hkv != 0, causal "
                               "with Nq > Nk, or too large for 32-bit indexing)";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128; decode chunk "
-                                    "must be a positive multiple of 64";
+                                    "and page size must be positive multiples of 64";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: decode workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";

@@ -69,6 +69,16 @@ __device__ __forceinline__ int dswz(int row) {
 // segment).
 struct Pos {
   int b, kvh, qg, L, nb, seg, i, S;
+  int page;  // paged caches: physical page holding the step's keys
+};
+
+// Paged KV cache ([LLM-basics] §8, PagedAttention): the keys of sequence b are kept in
+// pages of page_size keys, [num_pages, page_size, Hkv, d]; table[b * max_pages + j] is
+// the physical page of the sequence's logical page j.  page_size is a multiple of 64, so
+// a 64-key step never straddles two pages.  Unused by the contiguous-cache kernel.
+struct Paging {
+  const int* table;
+  int max_pages, page_size, num_pages;
 };
 
 // Steps per wave, computed identically by both kernels from the total step count T.
@@ -76,12 +86,12 @@ __device__ __forceinline__ int steps_per_wave(int T, int W, int rmin) {
   return max((T + W - 1) / W, rmin);
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint16_t* __restrict__ Qd, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int* __restrict__ seqlens, float* __restrict__ part_o,
     float* __restrict__ part_lse, int B, int Hq, int Hkv, int Nk_max, int rmin, int max_pieces,
-    int QG, float c) {
+    int QG, float c, Paging pg) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
   constexpr int VI = kStep * CH / 64;    // LDS-direct instructions per step
   constexpr int DB = D / 16;             // 16-row d blocks of O^T
@@ -164,6 +174,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     p.S = __builtin_amdgcn_readfirstlane(S);
     p.kvh = __builtin_amdgcn_readfirstlane(seg / QG);
     p.qg = __builtin_amdgcn_readfirstlane(seg % QG);
+    p.page = 0;
+    if constexpr (PAGED) {
+      // scalar load through the constant address space; entries are clamped into the
+      // pool so a bad table entry cannot address outside it
+      const __attribute__((address_space(4))) int* tb =
+          (const __attribute__((address_space(4))) int*)pg.table;
+      const int lp = __builtin_amdgcn_readfirstlane((i * kStep) / pg.page_size);
+      int e = tb[__builtin_amdgcn_readfirstlane(bb * pg.max_pages + lp)];
+      e = e < 0 ? 0 : (e >= pg.num_pages ? pg.num_pages - 1 : e);
+      p.page = __builtin_amdgcn_readfirstlane(e);
+    }
     return p;
   };
   // Position of global step g (0 <= g < T): skip whole sequences, then split the rest.
@@ -196,26 +217,48 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)(it.L - 1) * row_bytes + D * 2);
     return dmake_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nrec);
   };
+  // Paged caches: descriptor of the step's page for K/V head kvh, clipped after the
+  // page's last key inside the sequence (`valid` >= 1 keys).
+  auto page_rsrc = [&](const uint16_t* base, int page, int kvh, int valid)
+      __attribute__((always_inline)) {
+    const uint64_t a =
+        reinterpret_cast<uint64_t>(base + ((size_t)page * pg.page_size * Hkv + kvh) * D);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)(valid - 1) * row_bytes + D * 2);
+    return dmake_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nrec);
+  };
   // Issue the loads of step `it`: K into `kf`, V into LDS stage.  Every cache byte is
   // read once, so the loads are marked non-temporal.
   auto issue = [&](const Pos& it, u32x4 (*kf)[KS], auto stage_c)
       __attribute__((always_inline)) {
     constexpr int stage = decltype(stage_c)::value;
-    const __amdgpu_buffer_rsrc_t rk = rsrc_of(Kc, it);
-    const __amdgpu_buffer_rsrc_t rv = rsrc_of(Vc, it);
     const int n0 = it.i * kStep;
+    __amdgpu_buffer_rsrc_t rk, rv;
+    uint32_t soff;  // byte offset of the step's first key row inside the descriptor
+    if constexpr (PAGED) {
+      const int p0 = __builtin_amdgcn_readfirstlane((n0 / pg.page_size) * pg.page_size);
+      const int valid = min(pg.page_size, it.L - p0);
+      rk = page_rsrc(Kc, it.page, it.kvh, valid);
+      rv = page_rsrc(Vc, it.page, it.kvh, valid);
+      soff = (uint32_t)(n0 - p0) * row_bytes;
+    } else {
+      rk = rsrc_of(Kc, it);
+      rv = rsrc_of(Vc, it);
+      soff = (uint32_t)n0 * row_bytes;
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int st = 0; st < KS; ++st)
         kf[kb][st] = __builtin_amdgcn_raw_buffer_load_b128(
-            rk, k_lane + 64u * st, (uint32_t)(n0 + 16 * kb) * row_bytes, kNT);
+            rk, k_lane + 64u * st, soff + (uint32_t)(16 * kb) * row_bytes, kNT);
     uint16_t* dst = stage == 1 ? vst1[wave] : vst0[wave];
 #pragma unroll
     for (int i = 0; i < VI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rv, (dlds_void_t*)(dst + i * 512), 16, v_lane[i & 1],
-          (uint32_t)n0 * row_bytes + (uint32_t)(i & ~1) * (64 / CH) * row_bytes, 0, kNT);
+          soff + (uint32_t)(i & ~1) * (64 / CH) * row_bytes, 0, kNT);
   };
 
   auto item_begin = [&](const Pos& it) __attribute__((always_inline)) {
@@ -503,7 +546,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   if (threadIdx.x == 0) LSE[row] = (nc > 0) ? Mtr + fast_log2(St) * kLn2 : kNegInf;
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int QG = (G + 15) / 16;
@@ -515,10 +558,11 @@ hipError_t launch(const DecodeArgs& a, hipStream_t s) {
       cus = v;
   }
   const int rmin = a.chunk / kStep;  // a piece has at least `chunk` keys' worth of steps
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)cus), dim3(kThreads), 0, s,
+  const Paging pg{a.block_table, a.max_pages, a.page_size, a.num_pages};
+  hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)cus), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.seqlens, a.part_o, a.part_lse, a.B,
-                     a.Hq, a.Hkv, a.Nk_max, rmin, a.max_pieces, QG, a.scale * kLog2e);
+                     a.Hq, a.Hkv, a.Nk_max, rmin, a.max_pieces, QG, a.scale * kLog2e, pg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.Hq, (unsigned)a.B),
@@ -530,7 +574,9 @@ hipError_t launch(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t s) {
-  return a.d == 64 ? launch<64>(a, s) : launch<128>(a, s);
+  if (a.block_table != nullptr)
+    return a.d == 64 ? launch<64, true>(a, s) : launch<128, true>(a, s);
+  return a.d == 64 ? launch<64, false>(a, s) : launch<128, false>(a, s);
 }
 
 }  // namespace fa

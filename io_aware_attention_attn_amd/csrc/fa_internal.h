@@ -35,6 +35,10 @@ struct DecodeArgs {
   float* part_lse;
   int B, Hq, Hkv, Nk_max, d, chunk, max_pieces;
   float scale;
+  // paged caches (block_table != nullptr): k, v are [num_pages, page_size, Hkv, d] and
+  // Nk_max = max_pages * page_size
+  const int* block_table = nullptr;
+  int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);

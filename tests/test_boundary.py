@@ -36,7 +36,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(names) == {"fa_forward", "fa_forward_f32", "fa_decode_splitkv_workspace_bytes",
-                          "fa_decode_splitkv", "fa_status_str"}
+                          "fa_decode_splitkv", "fa_decode_paged", "fa_status_str"}
     for n in names:
         assert hasattr(L, n), f"libfa.so does not export {n}"
 
@@ -118,6 +118,35 @@ def _dec(L, q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nk_max=512, d=1
 ])
 def test_decode_rejects(L, kw, status):
     assert _dec(L, **kw) == status
+
+
+def _paged(L, q=P, kp=P, vp=P, bt=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, num_pages=16,
+           page_size=256, max_pages=4, d=128, scale=0.1, chunk=256, ws=P, ws_bytes=1 << 30):
+    return L.fa_decode_paged(q, kp, vp, bt, sl, o, lse, B, Hq, Hkv, num_pages, page_size,
+                             max_pages, d, scale, chunk, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kp=None), fa.FA_ERR_NULL),
+    (dict(vp=None), fa.FA_ERR_NULL),
+    (dict(bt=None), fa.FA_ERR_NULL),
+    (dict(sl=None), fa.FA_ERR_NULL),
+    (dict(num_pages=0), fa.FA_ERR_SHAPE),
+    (dict(page_size=0), fa.FA_ERR_SHAPE),
+    (dict(max_pages=0), fa.FA_ERR_SHAPE),
+    (dict(page_size=100), fa.FA_ERR_UNSUPPORTED),
+    (dict(page_size=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(max_pages=1 << 30, page_size=64), fa.FA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
+    (dict(d=100), fa.FA_ERR_UNSUPPORTED),
+    (dict(chunk=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(kp=MIS), fa.FA_ERR_ALIGN),
+    (dict(bt=0x10002), fa.FA_ERR_ALIGN),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), fa.FA_ERR_WORKSPACE),
+])
+def test_paged_decode_rejects(L, kw, status):
+    assert _paged(L, **kw) == status
 
 
 def test_binding_raises_without_gpu_tensors(L):

@@ -235,6 +235,88 @@ def test_decode_empty_sequences():
 
 
 # ---------------------------------------------------------------------------
+# paged KV-cache decode ([LLM-basics] §8, PagedAttention)
+# ---------------------------------------------------------------------------
+
+def _run_paged(q, kp, vp, table, lengths, scale, chunk):
+    dev = _dev()
+    B, Hq, d = q.shape
+    o = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev)
+    fa.fa_decode_paged(q.to(dev), kp.to(dev), vp.to(dev), table.to(dev), lengths.to(dev),
+                       scale=scale, chunk=chunk, o=o, lse=lse)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def test_c5_decode_paged_full():
+    """The c5 decode with its cache scattered over a permuted pool of 256-key pages."""
+    cfg = W.CONFIGS["c5"]
+    lengths, q, kc, vc = W.decode_inputs_for(cfg)
+    kp, vp, table = W.paged_from_contiguous(kc, vc, lengths, 256, seed=7, spare_pages=9)
+    o, lse = _run_paged(q, kp, vp, table, lengths, cfg.scale, cfg.chunk)
+    o_ref, lse_ref = oracle.decode_attention_paged(q, kp, vp, table, lengths, 256, cfg.scale)
+    _cmp(o, lse, o_ref, lse_ref, TOL_BF16, "c5 paged")
+
+
+PAGED = [  # B, Hq, Hkv, d, page_size, lengths, chunk
+    (3, 8, 2, 128, 64, [1, 64, 130], 64),
+    (4, 16, 2, 64, 128, [127, 128, 129, 600], 256),
+    (2, 8, 1, 128, 1024, [1000, 2500], 256),          # pages longer than a chunk
+    (70, 4, 1, 64, 64, [1 + (41 * i) % 300 for i in range(70)], 64),   # > 64 sequences
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=[str(c[:5]) for c in PAGED])
+def test_decode_paged_edges(case):
+    B, Hq, Hkv, d, ps, lens, chunk = case
+    lengths = torch.tensor(lens, dtype=torch.int32)
+    Nk_max = ((max(lens) + ps - 1) // ps) * ps
+    lengths, q, kc, vc = W.decode_inputs(B, Hq, Hkv, d, Nk_max, 0, 0, seed=21, lengths=lengths)
+    kp, vp, table = W.paged_from_contiguous(kc, vc, lengths, ps, seed=22, spare_pages=3)
+    scale = 1 / math.sqrt(d)
+    o, lse = _run_paged(q, kp, vp, table, lengths, scale, chunk)
+    o_ref, lse_ref = oracle.decode_attention_paged(q, kp, vp, table, lengths, ps, scale)
+    _cmp(o, lse, o_ref, lse_ref, TOL_BF16, f"paged {case[:5]}")
+
+
+def test_decode_paged_shared_pages():
+    """Sequences that share physical pages (a common prefix, as in the pages' block-table
+    figure) and an empty sequence (O = 0, LSE = -inf)."""
+    ps, Hq, Hkv, d = 64, 8, 2, 128
+    g = torch.Generator("cpu").manual_seed(31)
+    num_pages = 12
+    kp = torch.randn((num_pages, ps, Hkv, d), generator=g).to(torch.bfloat16)
+    vp = torch.randn((num_pages, ps, Hkv, d), generator=g).to(torch.bfloat16)
+    table = torch.tensor([[4, 9, 1, 7, -1], [4, 9, 2, -1, -1], [4, 9, 1, 7, 11], [0, -1, -1, -1, -1],
+                          [5, 3, -1, -1, -1]], dtype=torch.int32)
+    lens = [230, 150, 300, 0, 128]
+    lengths = torch.tensor(lens, dtype=torch.int32)
+    q = torch.randn((len(lens), Hq, d), generator=g).to(torch.bfloat16)
+    o, lse = _run_paged(q, kp, vp, table, lengths, 1 / math.sqrt(d), 64)
+    live = [b for b, L in enumerate(lens) if L > 0]
+    o_ref, lse_ref = oracle.decode_attention_paged(q, kp, vp, table, lengths, ps, 1 / math.sqrt(d),
+                                                   batches=live)
+    _cmp(o[live], lse[live], o_ref[live], lse_ref[live], TOL_BF16, "paged shared")
+    assert torch.all(o[3] == 0) and torch.all(lse[3] == float("-inf"))
+
+
+def test_decode_paged_matches_contiguous():
+    """Same keys through a page table and through the contiguous cache: the two entry points
+    agree to fp32 rounding (the split and the merge are the same; only addressing differs)."""
+    cfg = W.CONFIGS["c5"]
+    lengths, q, kc, vc = W.decode_inputs(4, 64, 8, 128, 4096, 1000, 4096, seed=41)
+    kp, vp, table = W.paged_from_contiguous(kc, vc, lengths, 128, seed=42)
+    o1, l1 = _run_paged(q, kp, vp, table, lengths, cfg.scale, 256)
+    dev = _dev()
+    o2, l2 = fa.fa_decode_splitkv(q.to(dev), kc.to(dev), vc.to(dev), lengths.to(dev),
+                                  scale=cfg.scale, chunk=256)
+    torch.cuda.synchronize()
+    assert (o1 - o2.cpu()).abs().max().item() <= 1e-6
+    assert (l1 - l2.cpu()).abs().max().item() <= 1e-6
+
+
+# ---------------------------------------------------------------------------
 # determinism and stream behaviour
 # ---------------------------------------------------------------------------
 
