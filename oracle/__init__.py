@@ -22,6 +22,7 @@ inputs, a library routine).  No function here is "parity unpinned".
 from .attention import (  # noqa: F401
     attention,
     attention_probs,
+    attention_varlen,
     decode_attention,
     decode_attention_paged,
     lse_merge,

@@ -189,6 +189,34 @@ def decode_attention_paged(q, k_pages, v_pages, block_table, lengths, page_size:
     return o, lse
 
 
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool,
+                     heads: Optional[Sequence[int]] = None):
+    """Attention over a batch of variable-length sequences packed along the token axis.
+
+    [FA3-entry] §2 lists variable-length inputs among the supported attention forms;
+    [FA-evo] "실전 구현" shows the per-batch [B, S, H, D] layout this packs.  q is
+    [total_q, Hq, d] and k, v are [total_k, Hkv, d]; sequence b owns query rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and key rows cu_seqlens_k[b] ..
+    cu_seqlens_k[b+1] - 1, and attends only within itself: each sequence is the
+    standard attention of ``attention`` (causal alignment per sequence, bottom-right).
+    Returns O [total_q, Hq, d] and LSE [Hq, total_q] in float64.
+    """
+    total_q, Hq, d = q.shape
+    o = torch.full((total_q, Hq, d), float("nan"), dtype=f64)
+    lse = torch.full((Hq, total_q), float("nan"), dtype=f64)
+    B = len(cu_seqlens_q) - 1
+    for b in range(B):
+        q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
+        if q1 == q0:
+            continue
+        ob, lb = attention(q[q0:q1].unsqueeze(0), k[k0:k1].unsqueeze(0), v[k0:k1].unsqueeze(0),
+                           scale, causal, heads=heads)
+        o[q0:q1] = ob[0]
+        lse[:, q0:q1] = lb[0]
+    return o, lse
+
+
 def online_softmax_update(m_prev: torch.Tensor, l_prev: torch.Tensor, acc_prev: torch.Tensor,
                           s_block: torch.Tensor, v_block: torch.Tensor):
     """One block step of the online softmax, per row.

@@ -409,6 +409,53 @@ def pin_paged_dominant_key(orc):
             _close(lse[0, h:h + 1], [60.0 + 0.0], 1e-12, f"dominant paged LSE t={t}")
 
 
+def pin_varlen_constant_v(orc):
+    """Packed variable-length batch: every value row of sequence b equals a constant
+    vector c_b, so every output row of sequence b is c_b whatever the scores — any
+    read of another sequence's keys or values, or a wrong row offset, shows."""
+    lens_q = [3, 1, 5, 2]
+    lens_k = [4, 1, 5, 7]
+    Hq, Hkv, d = 4, 2, 3
+    cu_q = [0] + list(torch.cumsum(torch.tensor(lens_q), 0).tolist())
+    cu_k = [0] + list(torch.cumsum(torch.tensor(lens_k), 0).tolist())
+    q = _rand((cu_q[-1], Hq, d), 150)
+    k = _rand((cu_k[-1], Hkv, d), 151, 2.0)
+    v = torch.empty((cu_k[-1], Hkv, d), dtype=f64)
+    consts = [_rand((Hkv, d), 152 + b) for b in range(4)]
+    for b in range(4):
+        v[cu_k[b]:cu_k[b + 1]] = consts[b]
+    for causal in (False, True):
+        o, lse = orc.attention_varlen(q, k, v, cu_q, cu_k, 0.5, causal)
+        for b in range(4):
+            for r in range(cu_q[b], cu_q[b + 1]):
+                for h in range(Hq):
+                    _close(o[r, h], consts[b][h // (Hq // Hkv)], 1e-14, f"varlen const b={b}")
+        assert torch.isfinite(lse).all()
+
+
+def pin_varlen_causal_alignment(orc):
+    """With K = 0 every visible key scores 0, so a row's output is the mean of the V rows
+    it sees and LSE = ln(count).  Per sequence, causal row i sees keys 0 .. i + (Nk_b - Nq_b)
+    (bottom-right alignment inside the sequence, not across the pack)."""
+    lens_q = [2, 4, 1]
+    lens_k = [5, 4, 3]
+    Hq, Hkv, d = 2, 1, 2
+    cu_q = [0, 2, 6, 7]
+    cu_k = [0, 5, 9, 12]
+    q = _rand((7, Hq, d), 160)
+    k = torch.zeros((12, Hkv, d), dtype=f64)
+    v = _rand((12, Hkv, d), 161)
+    o, lse = orc.attention_varlen(q, k, v, cu_q, cu_k, 1.0, True)
+    for b in range(3):
+        nq, nk = lens_q[b], lens_k[b]
+        for i in range(nq):
+            cnt = i + (nk - nq) + 1
+            want = v[cu_k[b]:cu_k[b] + cnt, 0].mean(dim=0)
+            for h in range(Hq):
+                _close(o[cu_q[b] + i, h], want, 1e-14, f"varlen causal b={b} i={i}")
+                _close(lse[h, cu_q[b] + i:cu_q[b] + i + 1], [math.log(cnt)], 1e-14, "varlen LSE")
+
+
 # ---------------------------------------------------------------------------
 # independent re-computations
 # ---------------------------------------------------------------------------
@@ -472,6 +519,8 @@ def pin_sdpa_crosscheck(orc):
 
 
 ALL_PINS = [
+    pin_varlen_constant_v,
+    pin_varlen_causal_alignment,
     pin_paged_constant_pages,
     pin_paged_dominant_key,
     pin_worked_example_printed,

@@ -39,6 +39,12 @@ MUTANTS = {
     "decode reads one row short": ("L = int(lengths[b])\n        kk = _as64(k_cache[b, :L])",
                                    "L = max(int(lengths[b]) - 1, 1)\n        kk = _as64(k_cache[b, :L])"),
     "decode reads past length": ("kk = _as64(k_cache[b, :L])", "kk = _as64(k_cache[b, :L + 1])"),
+    "varlen keys from the query offsets": ("ob, lb = attention(q[q0:q1].unsqueeze(0), k[k0:k1].unsqueeze(0), v[k0:k1]",
+                                          "ob, lb = attention(q[q0:q1].unsqueeze(0), k[q0:q1].unsqueeze(0), v[q0:q1]"),
+    "varlen values of the next sequence": ("v[k0:k1].unsqueeze(0),\n                           scale, causal, heads=heads)",
+                                           "v[k1:k1 + (k1 - k0)].unsqueeze(0),\n                           scale, causal, heads=heads)"),
+    "varlen whole-pack causal alignment": ("ob, lb = attention(q[q0:q1].unsqueeze(0), k[k0:k1].unsqueeze(0), v[k0:k1].unsqueeze(0),\n                           scale, causal, heads=heads)",
+                                           "ob, lb = attention(q[q0:q1].unsqueeze(0), k[:k1].unsqueeze(0), v[:k1].unsqueeze(0),\n                           scale, causal, heads=heads)"),
     "paged ignores block table": ("page = int(block_table[b][j])", "page = j"),
     "paged reads whole last page": ("n = min(page_size, L - j * page_size)", "n = page_size"),
     "paged misses partial last page": ("for j in range((L + page_size - 1) // page_size):",
