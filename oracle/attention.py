@@ -199,7 +199,9 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
     cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and key rows cu_seqlens_k[b] ..
     cu_seqlens_k[b+1] - 1, and attends only within itself: each sequence is the
     standard attention of ``attention`` (causal alignment per sequence, bottom-right).
-    Returns O [total_q, Hq, d] and LSE [Hq, total_q] in float64.
+    Returns O [total_q, Hq, d] and LSE [Hq, total_q] in float64.  A sequence with no
+    keys has no softmax to take (the row max and the normaliser of [LLM-basics] ③-1
+    are over an empty set): its rows are left NaN, as are causal rows that see no key.
     """
     total_q, Hq, d = q.shape
     o = torch.full((total_q, Hq, d), float("nan"), dtype=f64)
@@ -208,7 +210,7 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
     for b in range(B):
         q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
         k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])
-        if q1 == q0:
+        if q1 == q0 or k1 == k0:
             continue
         ob, lb = attention(q[q0:q1].unsqueeze(0), k[k0:k1].unsqueeze(0), v[k0:k1].unsqueeze(0),
                            scale, causal, heads=heads)

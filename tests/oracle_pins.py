@@ -433,6 +433,36 @@ def pin_varlen_constant_v(orc):
         assert torch.isfinite(lse).all()
 
 
+def pin_varlen_empty_sequences(orc):
+    """Sequences with no queries or no keys inside a pack: a sequence without queries
+    still moves the key offsets of those after it, and a sequence without keys has no
+    defined softmax (its rows stay NaN).  Constant per-sequence V rows make every
+    defined output row known in closed form."""
+    lens_q = [2, 0, 3, 4, 1]
+    lens_k = [0, 4, 3, 1, 2]
+    Hq, Hkv, d = 2, 1, 3
+    cu_q = [0, 2, 2, 5, 9, 10]
+    cu_k = [0, 0, 4, 7, 8, 10]
+    q = _rand((10, Hq, d), 170)
+    k = _rand((10, Hkv, d), 171)
+    v = torch.empty((10, Hkv, d), dtype=f64)
+    consts = [_rand((Hkv, d), 172 + b) for b in range(5)]
+    for b in range(5):
+        v[cu_k[b]:cu_k[b + 1]] = consts[b]
+    o, lse = orc.attention_varlen(q, k, v, cu_q, cu_k, 0.7, False)
+    assert torch.isnan(o[0:2]).all() and torch.isnan(lse[:, 0:2]).all(), "keyless rows must stay NaN"
+    for b in (2, 3, 4):
+        for r in range(cu_q[b], cu_q[b + 1]):
+            for h in range(Hq):
+                _close(o[r, h], consts[b][0], 1e-14, f"varlen empty-seq offsets b={b}")
+    assert torch.isfinite(lse[:, 2:]).all()
+    # a one-key sequence: LSE is that key's score exactly
+    r = cu_q[3]
+    for h in range(Hq):
+        want = 0.7 * float(q[r, h] @ k[cu_k[3], 0])
+        _close(lse[h, r:r + 1], [want], 1e-13, "varlen single-key LSE")
+
+
 def pin_varlen_causal_alignment(orc):
     """With K = 0 every visible key scores 0, so a row's output is the mean of the V rows
     it sees and LSE = ln(count).  Per sequence, causal row i sees keys 0 .. i + (Nk_b - Nq_b)
@@ -521,6 +551,7 @@ def pin_sdpa_crosscheck(orc):
 ALL_PINS = [
     pin_varlen_constant_v,
     pin_varlen_causal_alignment,
+    pin_varlen_empty_sequences,
     pin_paged_constant_pages,
     pin_paged_dominant_key,
     pin_worked_example_printed,

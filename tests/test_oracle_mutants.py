@@ -45,6 +45,9 @@ MUTANTS = {
                                            "v[k1:k1 + (k1 - k0)].unsqueeze(0),\n                           scale, causal, heads=heads)"),
     "varlen whole-pack causal alignment": ("ob, lb = attention(q[q0:q1].unsqueeze(0), k[k0:k1].unsqueeze(0), v[k0:k1].unsqueeze(0),\n                           scale, causal, heads=heads)",
                                            "ob, lb = attention(q[q0:q1].unsqueeze(0), k[:k1].unsqueeze(0), v[:k1].unsqueeze(0),\n                           scale, causal, heads=heads)"),
+    "varlen key count from the query count": ("k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])",
+                                              "k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b]) + (q1 - q0)"),
+    "varlen keyless sequence not skipped": ("if q1 == q0 or k1 == k0:", "if q1 == q0:"),
     "paged ignores block table": ("page = int(block_table[b][j])", "page = j"),
     "paged reads whole last page": ("n = min(page_size, L - j * page_size)", "n = page_size"),
     "paged misses partial last page": ("for j in range((L + page_size - 1) // page_size):",
