@@ -9,7 +9,9 @@ One step = one pass of the whole hot path on resident synthetic inputs:
     the merge kernel.
 `value` is the prefill's algorithmic TFLOP/s (4*B*Hq*Nq*Nk*d / 2 for causal) over
 its measured kernel time; the decode's HBM GB/s (compulsory K/V/q/O/LSE bytes)
-is reported alongside.  Kernel times come from HIP events recorded on the
+is reported alongside, and so are the paged-KV decode and the packed variable-length
+prefill (16 causal GQA sequences, lengths ~U[512, 16384], one launch), each timed on
+its own after the step.  Kernel times come from HIP events recorded on the
 stream the kernels are launched on (torch's current stream), around every
 launch of the timed region.
 
@@ -43,6 +45,9 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-KV decode measurement (reported beside the step)")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed variable-length prefill measurement (reported beside "
+                         "the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -154,6 +159,47 @@ def bench_paged(fa, W, dcfg, dec, dev, K, page_size=256):
             "median_call_ms": round(sorted(ms)[K // 2], 4), "page_size": page_size,
             "pool_pages": int(kp.shape[0]),
             "layout": "c5 keys in a seeded permutation of a page pool, block table per sequence"}
+
+
+def bench_varlen(fa, W, dev, K):
+    """The packed variable-length prefill (16 causal GQA sequences of U[512, 16384] tokens in
+    one launch), timed on its own after the step; algorithmic TFLOP/s summed per sequence."""
+    import torch
+    cfg = W.VARLEN["v1"]
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    lengths, cu_q, cu_k, q, k, v = W.varlen_inputs_for(cfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    cqd, ckd = cu_q.to(dev), cu_k.to(dev)
+    tq = int(cu_q[-1])
+    o = torch.empty((tq, cfg.Hq, cfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.Hq, tq), dtype=torch.float32, device=dev)
+    max_q = int(lengths.max())
+
+    def call():
+        fa.fa_forward_varlen(qd, kd, vd, cqd, ckd, max_q, max_q, scale=cfg.scale,
+                             causal=cfg.causal, o=o, lse=lse)
+    print("[bench] packed varlen prefill", file=sys.stderr, flush=True)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / K
+    flops = W.varlen_flops(lengths, lengths, cfg.Hq, cfg.d, cfg.causal)
+    tf = flops / (avg * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
+            "median_launch_ms": round(sorted(ms)[K // 2], 4), "flop_per_launch": flops,
+            "workload": cfg.workload, "total_tokens": tq, "max_seqlen": max_q,
+            "kernel": "prefill_bf16_kernel<128, causal, varlen>"}
 
 
 def cpu_baseline_decode(cfg, lengths, q, kc, vc, target_s):
@@ -306,6 +352,10 @@ def main():
                             "traffic_merge": profiled_traffic("decode_merge_kernel<128>")}
     if dec and not args.no_paged:
         result["decode_paged"] = bench_paged(fa, W, dcfg, dec, dev, K)
+    if not args.no_varlen:
+        del qd, kd, vd, o, lse
+        torch.cuda.empty_cache()
+        result["prefill_varlen"] = bench_varlen(fa, W, dev, K)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_prefill(pcfg, args.cpu_seconds)

@@ -63,7 +63,8 @@ typedef enum {
                               sizes whose element counts overflow 32-bit row indexing */
   FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}; decode chunk or page size not a positive
                               multiple of 64 */
-  FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned (or a packed row
+                              stride is not a multiple of 8 elements) */
   FA_ERR_WORKSPACE = -5,   /* decode workspace missing or smaller than required */
   FA_ERR_HIP = -6          /* the kernel launch failed (hipGetLastError) */
 } fa_status;
@@ -102,6 +103,48 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                    hipStream_t stream);
+
+/*
+ * fa_forward_varlen — fa_forward over a batch of variable-length sequences packed
+ * along the token axis, bf16 inputs.
+ *
+ * [FA3-entry] §2 lists variable-length inputs among the supported attention forms.
+ * Sequence b owns query tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and key/value
+ * tokens cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1 and attends only within itself; each
+ * sequence is computed exactly as fa_forward computes one batch entry (the same
+ * kernel, causal alignment to the end of that sequence's keys).  No padding is read
+ * or computed.
+ *
+ *   q              bf16, token t, head h at q[t * q_row_stride + h * d + i]   (read)
+ *   k, v           bf16, token t, head h at k[t * k_row_stride + h * d + i]   (read)
+ *                  (a stride larger than H*d lets q, k, v be views of one packed
+ *                  [total, Hq + 2 Hkv, d] QKV tensor)
+ *   cu_seqlens_q   int32 [B + 1] on the device, non-decreasing, 0 .. total_q
+ *   cu_seqlens_k   int32 [B + 1] on the device, non-decreasing, 0 .. total_k
+ *                  (the kernel clamps both into range for memory safety)
+ *   o              fp32 [total_q, Hq, d]   (written for every token of every sequence)
+ *   lse            fp32 [Hq, total_q]      (written likewise)
+ *   max_seqlen_q   longest query sequence, >= 1 (sizes the grid)
+ *   max_seqlen_k   longest key sequence, >= 0.  Both are the caller's bound: a sequence
+ *                  longer than either is cut to it (only its first max_seqlen_q queries
+ *                  are written and its first max_seqlen_k keys read), never read past.
+ *                  Byte offsets inside one sequence are 32-bit, so (max_seqlen + 256) *
+ *                  row_stride * 2 must stay below 2^31 (FA_ERR_SHAPE); the pack as a whole
+ *                  may be larger.
+ *   total_q        rows of q, o and lse; total_k: rows of k and v (0 allowed)
+ *   q_row_stride   elements between consecutive tokens of q: >= Hq * d, a multiple of 8
+ *   k_row_stride   likewise for k, >= Hkv * d; v_row_stride must equal it
+ *   causal         0 or 1; key j of a sequence is visible from its query i iff
+ *                  j <= i + (Nk_b - Nq_b)
+ * A query that sees no key (a sequence with no keys, or under causal masking a query
+ * ahead of all keys when Nq_b > Nk_b) gets O = 0 and LSE = -inf.  The cu_seqlens
+ * arrays need 4-byte alignment.  Returns FA_OK or a negative fa_status.
+ */
+int fa_forward_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                      int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
+                      float scale, int causal, int q_row_stride, int k_row_stride,
+                      int v_row_stride, hipStream_t stream);
 
 /*
  * fa_decode_splitkv_workspace_bytes — bytes of device workspace that

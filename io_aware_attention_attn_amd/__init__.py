@@ -9,6 +9,8 @@ of the computation runs in the library's HIP kernels; there is no fallback path.
 Functions (same names as the C entry points):
   fa_forward(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None)
   fa_forward_f32(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None)
+  fa_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    scale=None, causal=False, o=None, lse=None, stream=None)
   fa_decode_splitkv_workspace_bytes(B, Hq, Nk_max, d, chunk=256)
   fa_decode_splitkv(q, k_cache, v_cache, seqlens_k, scale=None, chunk=256, o=None,
                     lse=None, workspace=None, stream=None)
@@ -57,6 +59,9 @@ def lib() -> ctypes.CDLL:
     L.fa_forward.restype = i
     L.fa_forward_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     L.fa_forward_f32.restype = i
+    L.fa_forward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i,
+                                    i, i, i, vp]
+    L.fa_forward_varlen.restype = i
     L.fa_decode_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
     L.fa_decode_splitkv_workspace_bytes.restype = sz
     L.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -136,6 +141,57 @@ def fa_forward_f32(q, k, v, scale: Optional[float] = None, causal: bool = False,
     """fp32 variant of fa_forward (no 16-bit rounding anywhere)."""
     import torch
     return _forward(lib().fa_forward_f32, q, k, v, scale, causal, o, lse, stream, torch.float32)
+
+
+def _check_token_rows(t, name):
+    """[total, H, d] bf16 GPU tensor whose tokens may be strided (a view of a packed
+    QKV tensor) but whose heads and head dims are dense."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_cuda:
+        raise ValueError(f"{name} must be a 3-dim bf16 GPU tensor, got {t.dtype} {tuple(t.shape)}")
+    if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name}: heads and head dims must be dense (strides {t.stride()})")
+
+
+def fa_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                      max_seqlen_k: int, scale: Optional[float] = None, causal: bool = False, o=None, lse=None,
+                      stream=None):
+    """Packed variable-length batch: q bf16 [total_q,Hq,d], k/v bf16 [total_k,Hkv,d] (token
+    stride free, e.g. views of one QKV tensor), cu_seqlens_q/k int32 [B+1] on the GPU
+    -> (O fp32 [total_q,Hq,d], LSE fp32 [Hq,total_q])."""
+    import torch
+    _check_token_rows(q, "q")
+    _check_token_rows(k, "k")
+    _check_token_rows(v, "v")
+    _check_tensor(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _check_tensor(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk = k.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if (tuple(v.shape) != tuple(k.shape) or dk != d or cu_seqlens_k.shape[0] != B + 1
+            or v.stride(0) != k.stride(0)):
+        raise ValueError(f"varlen shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} "
+                         f"v {tuple(v.shape)} cu {B + 1}/{cu_seqlens_k.shape[0]}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((total_q, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    _check_tensor(o, "o", torch.float32, 3)
+    _check_tensor(lse, "lse", torch.float32, 2)
+    if tuple(o.shape) != (total_q, Hq, d) or tuple(lse.shape) != (Hq, total_q):
+        raise ValueError("o / lse have the wrong shape")
+    st = lib().fa_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                 _ptr(cu_seqlens_k), B, Hq, Hkv, int(max_seqlen_q),
+                                 int(max_seqlen_k), total_q,
+                                 total_k, d, float(scale), 1 if causal else 0, q.stride(0),
+                                 k.stride(0), v.stride(0), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward_varlen")
+    return o, lse
 
 
 def fa_decode_splitkv_workspace_bytes(B: int, Hq: int, Nk_max: int, d: int, chunk: int = 256) -> int:

@@ -75,6 +75,42 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
   return fa::launch_prefill_f32(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_forward_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                      int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
+                      float scale, int causal, int q_row_stride, int k_row_stride,
+                      int v_row_stride, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_seqlen_q <= 0 || max_seqlen_k < 0 || total_q <= 0 ||
+      total_k < 0 || d <= 0)
+    return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0 || max_seqlen_q > total_q || max_seqlen_k > total_k) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // token rows must hold all heads and start on 16-byte boundaries; K and V share one stride
+  if (q_row_stride < Hq * d || k_row_stride < Hkv * d || k_row_stride != v_row_stride)
+    return FA_ERR_SHAPE;
+  if (q_row_stride % 8 != 0 || k_row_stride % 8 != 0) return FA_ERR_ALIGN;
+  // 32-bit grid, and 32-bit byte offsets inside one sequence's rows (reads may run one
+  // block past its end; each sequence is addressed from its own first token)
+  if ((long long)B * Hq * ((max_seqlen_q + 127) / 128) > INT_MAX) return FA_ERR_SHAPE;
+  if ((long long)(max_seqlen_q + 256) * q_row_stride * 2 > INT_MAX ||
+      (long long)(max_seqlen_k + 256) * k_row_stride * 2 > INT_MAX)
+    return FA_ERR_SHAPE;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_ALIGN;
+  fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, scale,
+                    causal ? 1 : 0};
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.q_stride = q_row_stride;
+  a.kv_stride = k_row_stride;
+  return fa::launch_prefill_bf16(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int chunk) {
   if (check_decode_sizes(B, Hq, 1, Nk_max, d, chunk) != FA_OK) return 0;
   const int mp = max_pieces_of(Nk_max, chunk);
@@ -143,10 +179,11 @@ const char* fa_status_str(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (non-positive, Hq % Hkv != 0, causal "
-                              "with Nq > Nk, or too large for 32-bit indexing)";
+                              "with Nq > Nk, a packed row stride too small, or too large for 32-bit indexing)";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128; decode chunk "
                                     "and page size must be positive multiples of 64";
-    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a tensor pointer is not 16-byte aligned (or a "
+                              "packed row stride is not a multiple of 8 elements)";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: decode workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
     default: return "unknown fa_status";

@@ -18,6 +18,11 @@ struct PrefillArgs {
   int B, Hq, Hkv, Nq, Nk, d;
   float scale;
   int causal;
+  // variable-length packed batch (cu_q != nullptr): Nq / Nk = longest query / key sequence;
+  // q/k/v rows `*_stride` elements apart, O [total_q, Hq, d], LSE [Hq, total_q]
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int total_q = 0, total_k = 0, q_stride = 0, kv_stride = 0;
 };
 
 // Split-KV decode: q [B,Hq,d], caches [B,Nk_max,Hkv,d], seqlens [B] (device),

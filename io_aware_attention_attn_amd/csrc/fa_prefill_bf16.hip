@@ -118,13 +118,25 @@ __device__ __forceinline__ int xcd_remap(int g, int T) {
   return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-template <int D, int WAVES, bool CAUSAL>
+// Variable-length batches packed along the token axis ([FA3-entry] §2): sequence b owns
+// query rows cu_q[b] .. cu_q[b+1] - 1 and key rows cu_k[b] .. cu_k[b+1] - 1 (offsets are
+// clamped into [0, total], lengths to the kernel's Nq / Nk, which then hold the longest
+// query and key sequence); consecutive tokens are `*_stride` elements apart, which also
+// lets Q/K/V be views into one packed QKV tensor.  O is [total_q, Hq, d], LSE [Hq, total_q].
+struct Varlen {
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+  int q_stride, kv_stride;
+};
+
+template <int D, int WAVES, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64),
                           amdgpu_waves_per_eu(2, 2))) void
 prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     const uint16_t* __restrict__ V, float* __restrict__ O,
                     float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk, float c,
-                    int n_mblocks) {
+                    int n_mblocks, Varlen vl) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int BM = 32 * WAVES;
   constexpr int NT = WAVES * 64;
@@ -148,23 +160,84 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   const int G = Hq / Hkv;
   const int T = n_mblocks * B * Hq;
   const int lam = xcd_remap((int)blockIdx.x, T);
-  const int hg = lam % G;
-  const int rest = lam / G;
-  const int mb = n_mblocks - 1 - rest % n_mblocks;
-  const int bk = rest / n_mblocks;
-  const int kvh = bk % Hkv;
-  const int b = bk / Hkv;
+  int hg, mb, kvh, b;
+  if (!VARLEN) {
+    // equal sequences: (batch, K/V head) major, the group's heads adjacent per query block
+    hg = lam % G;
+    const int rest = lam / G;
+    mb = n_mblocks - 1 - rest % n_mblocks;
+    const int bk = rest / n_mblocks;
+    kvh = bk % Hkv;
+    b = bk / Hkv;
+  } else if (Hkv % kNumXcd == 0) {
+    // unequal sequences: K/V head major, so each XCD's contiguous slice holds whole K/V
+    // heads of every sequence (equal work per XCD), the group's heads adjacent
+    hg = lam % G;
+    const int rest = lam / G;
+    mb = n_mblocks - 1 - rest % n_mblocks;
+    const int bk = rest / n_mblocks;
+    b = bk % B;
+    kvh = bk / B;
+  } else {
+    // fewer K/V heads than XCDs: query head major (balanced when Hq is a multiple of 8)
+    mb = n_mblocks - 1 - lam % n_mblocks;
+    const int rest = lam / n_mblocks;
+    b = rest % B;
+    const int h = rest / B;
+    hg = h % G;
+    kvh = h / G;
+  }
   const int hq = kvh * G + hg;
   const int m0 = mb * BM;
 
-  const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
-  const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + ((size_t)b * Nq * Hq + hq) * D,
-                                              (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + ((size_t)b * Nk * Hkv + kvh) * D,
-                                              (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + ((size_t)b * Nk * Hkv + kvh) * D,
-                                              (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
+  // ---- this sequence's rows: fixed-length batch, or a slice of the packed batch
+  uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
+  uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
+  const uint16_t* Qb = Q + ((size_t)b * Nq * Hq + hq) * D;
+  const uint16_t* Kb = K + ((size_t)b * Nk * Hkv + kvh) * D;
+  const uint16_t* Vb = V + ((size_t)b * Nk * Hkv + kvh) * D;
+  size_t o_row0 = (size_t)b * Nq;                 // O row of this sequence's query 0
+  size_t lse0 = ((size_t)b * Hq + hq) * Nq;      // LSE index of this sequence's query 0
+  if constexpr (VARLEN) {
+    const __attribute__((address_space(4))) int* cq = (const __attribute__((address_space(4))) int*)vl.cu_q;
+    const __attribute__((address_space(4))) int* ck = (const __attribute__((address_space(4))) int*)vl.cu_k;
+    const int q0 = min(max(cq[b], 0), vl.total_q);
+    const int q1 = min(max(cq[b + 1], q0), vl.total_q);
+    const int k0 = min(max(ck[b], 0), vl.total_k);
+    const int k1 = min(max(ck[b + 1], k0), vl.total_k);
+    Nq = __builtin_amdgcn_readfirstlane(min(q1 - q0, Nq));
+    Nk = __builtin_amdgcn_readfirstlane(min(k1 - k0, Nk));
+    if (m0 >= Nq) return;  // the whole block is past this sequence's end
+    q_row_bytes = (uint32_t)vl.q_stride * 2;
+    kv_row_bytes = (uint32_t)vl.kv_stride * 2;
+    Qb = Q + (size_t)q0 * vl.q_stride + (size_t)hq * D;
+    Kb = K + (size_t)k0 * vl.kv_stride + (size_t)kvh * D;
+    Vb = V + (size_t)k0 * vl.kv_stride + (size_t)kvh * D;
+    o_row0 = (size_t)q0;
+    lse0 = (size_t)hq * vl.total_q + q0;
+  }
+  // ---- key blocks to visit
+  const int diag = Nk - Nq;  // key j visible from row i iff j <= i + diag
+  int kend = Nk;
+  if (CAUSAL) kend = min(Nk, min(m0 + BM, Nq) - 1 + diag + 1);
+  const int n = (kend + kBN - 1) / kBN;
+  if constexpr (VARLEN) {
+    if (n <= 0) {
+      // no key visible from any row of the block (no keys, or causal with more queries
+      // than keys): the rows' softmax is empty -> O = 0, LSE = -inf
+      const int r = m0 + tid / 2;  // two threads per row, D/2 columns each
+      if (tid < 2 * BM && r < Nq) {
+        float* Orow = O + ((o_row0 + r) * Hq + hq) * D + (tid & 1) * (D / 2);
+#pragma unroll
+        for (int i = 0; i < D / 2; i += 4) *reinterpret_cast<f32x4*>(Orow + i) = f32x4{};
+        if ((tid & 1) == 0) LSE[lse0 + r] = kNegInf;
+      }
+      return;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qb, (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kb, (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vb, (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
 
   // ---- Q^T fragments: lane holds query row qrow, d = 16*s + 8*hi .. +7 (zeros past Nq)
   const int qrow = m0 + wave * 32 + l32;
@@ -175,12 +248,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
         rq, (uint32_t)qrow * q_row_bytes + (uint32_t)(16 * s + 8 * hi) * 2, 0, 0);
     qf[s] = __builtin_bit_cast(bf16x8, w);
   }
-
-  // ---- key blocks to visit
-  const int diag = Nk - Nq;  // key j visible from row i iff j <= i + diag
-  int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(m0 + BM, Nq) - 1 + diag + 1);
-  const int n = (kend + kBN - 1) / kBN;
 
   // ---- per-lane LDS byte offsets of the MFMA operand reads
   // K (A of S^T): row kb*32 + l32, logical chunk 2*st + hi.
@@ -386,9 +453,11 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
   const float l_tot = xor32_sum(l_run);
   const float l_ex = xor32_sum(l_lse);
-  const float inv = 1.f / l_tot;
+  // a row that saw no key (packed batches only: an empty sequence, or causal rows ahead
+  // of every key) has l = 0 and acc = 0: O = 0, LSE = -inf
+  const float inv = (!VARLEN || l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (qrow < Nq) {
-    float* Orow = O + ((size_t)(b * Nq + qrow) * Hq + hq) * D;
+    float* Orow = O + ((o_row0 + qrow) * Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -397,28 +466,34 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
                    acc[db][4 * g + 3] * inv};
         *reinterpret_cast<f32x4*>(Orow + 32 * db + 8 * g + 4 * hi) = w;
       }
-    if (hi == 0) LSE[((size_t)b * Hq + hq) * Nq + qrow] = (m_ref + fast_log2(l_ex)) * kLn2;
+    if (hi == 0) LSE[lse0 + qrow] = (l_ex > 0.f) ? (m_ref + fast_log2(l_ex)) * kLn2 : kNegInf;
   }
   (void)NT;
 }
 
-template <int D, int WAVES, bool CAUSAL>
+template <int D, int WAVES, bool CAUSAL, bool VARLEN>
 hipError_t launch(const PrefillArgs& a, hipStream_t s) {
   constexpr int BM = 32 * WAVES;
+  // varlen: Nq / Nk are the longest query / key sequence (Nq sizes the grid)
   const int n_mblocks = (a.Nq + BM - 1) / BM;
   const long long blocks = (long long)n_mblocks * a.B * a.Hq;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, WAVES, CAUSAL>), dim3((unsigned)blocks),
+  const Varlen vl{a.cu_q, a.cu_k, a.total_q, a.total_k, a.q_stride, a.kv_stride};
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, WAVES, CAUSAL, VARLEN>), dim3((unsigned)blocks),
                      dim3(WAVES * 64), 0, s, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.o,
-                     a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_mblocks);
+                     a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_mblocks, vl);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? launch<64, 4, true>(a, s) : launch<64, 4, false>(a, s);
-  return a.causal ? launch<128, 4, true>(a, s) : launch<128, 4, false>(a, s);
+  if (a.cu_q != nullptr) {
+    if (a.d == 64) return a.causal ? launch<64, 4, true, true>(a, s) : launch<64, 4, false, true>(a, s);
+    return a.causal ? launch<128, 4, true, true>(a, s) : launch<128, 4, false, true>(a, s);
+  }
+  if (a.d == 64) return a.causal ? launch<64, 4, true, false>(a, s) : launch<64, 4, false, false>(a, s);
+  return a.causal ? launch<128, 4, true, false>(a, s) : launch<128, 4, false, false>(a, s);
 }
 
 }  // namespace fa

@@ -35,7 +35,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert set(names) == {"fa_forward", "fa_forward_f32", "fa_decode_splitkv_workspace_bytes",
+    assert set(names) == {"fa_forward", "fa_forward_f32", "fa_forward_varlen",
+                          "fa_decode_splitkv_workspace_bytes",
                           "fa_decode_splitkv", "fa_decode_paged", "fa_status_str"}
     for n in names:
         assert hasattr(L, n), f"libfa.so does not export {n}"
@@ -77,6 +78,46 @@ def _fwd(L, entry, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64
 ])
 def test_forward_rejects(L, entry, kw, status):
     assert _fwd(L, entry, **kw) == status
+
+
+def _varlen(L, q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, B=2, Hq=4, Hkv=2, max_q=64, max_k=70,
+            total_q=100, total_k=120, d=64, scale=0.125, causal=0, qs=None, ks=None, vs=None):
+    qs = Hq * d if qs is None else qs
+    ks = Hkv * d if ks is None else ks
+    vs = ks if vs is None else vs
+    return L.fa_forward_varlen(q, k, v, o, lse, cq, ck, B, Hq, Hkv, max_q, max_k, total_q,
+                               total_k, d, scale, causal, qs, ks, vs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(v=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(cq=None), fa.FA_ERR_NULL),
+    (dict(ck=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(max_q=0), fa.FA_ERR_SHAPE),
+    (dict(total_q=0, max_q=0), fa.FA_ERR_SHAPE),
+    (dict(max_q=101), fa.FA_ERR_SHAPE),          # longer than the whole pack
+    (dict(max_k=121), fa.FA_ERR_SHAPE),
+    (dict(max_k=-1), fa.FA_ERR_SHAPE),
+    (dict(total_k=-1), fa.FA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(qs=4 * 64 - 8), fa.FA_ERR_SHAPE),      # row narrower than its heads
+    (dict(ks=2 * 64 - 8, vs=2 * 64 - 8), fa.FA_ERR_SHAPE),
+    (dict(vs=3 * 64), fa.FA_ERR_SHAPE),          # K and V strides differ
+    (dict(qs=4 * 64 + 4), fa.FA_ERR_ALIGN),      # rows not 16-byte aligned
+    (dict(ks=2 * 64 + 4, vs=2 * 64 + 4), fa.FA_ERR_ALIGN),
+    (dict(k=MIS), fa.FA_ERR_ALIGN),
+    (dict(lse=MIS), fa.FA_ERR_ALIGN),
+    (dict(cq=0x10002), fa.FA_ERR_ALIGN),
+    # one sequence's rows past 2^31 bytes
+    (dict(total_q=1 << 22, max_q=1 << 17, Hq=64, Hkv=8, d=128), fa.FA_ERR_SHAPE),
+    (dict(total_k=1 << 22, max_k=1 << 20, Hq=64, Hkv=8, d=128), fa.FA_ERR_SHAPE),
+])
+def test_varlen_rejects(L, kw, status):
+    assert _varlen(L, **kw) == status
 
 
 def test_workspace_bytes(L):

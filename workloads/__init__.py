@@ -89,6 +89,40 @@ CONFIGS: Dict[str, object] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class VarlenConfig:
+    """A packed batch of B sequences whose lengths are uniform on [len_lo, len_hi]
+    (queries and keys of a sequence equally long, as in a prefill)."""
+    name: str
+    workload: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    len_lo: int
+    len_hi: int
+    causal: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+def varlen_flops(lens_q, lens_k, Hq: int, d: int, causal: bool) -> float:
+    """Algorithmic FLOPs of a packed batch: 4*Hq*d*sum_b(Nq_b*Nk_b), halved when causal
+    (the convention of PrefillConfig.flops, sequence by sequence)."""
+    f = 4.0 * Hq * d * sum(int(a) * int(b) for a, b in zip(lens_q, lens_k))
+    return f / 2.0 if causal else f
+
+
+# The packed variable-length prefill: a length mix of long-context GQA sequences in one launch.
+VARLEN: Dict[str, VarlenConfig] = {
+    "v1": VarlenConfig("v1", "causal GQA varlen prefill bf16 16 sequences L~U[512,16384] "
+                       "Hq=64 Hkv=8 d=128", B=16, Hq=64, Hkv=8, d=128, len_lo=512,
+                       len_hi=16384, causal=True),
+}
+
+
 def _round(x: torch.Tensor, dtype: str) -> torch.Tensor:
     if dtype == "bf16":
         return x.to(torch.bfloat16)
@@ -149,6 +183,47 @@ def decode_inputs(B: int, Hq: int, Hkv: int, d: int, Nk_max: int, lo: int, hi: i
 def decode_inputs_for(cfg: DecodeConfig, seed: int = 0, nan_pad: bool = True):
     return decode_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.Nk_max, cfg.len_lo, cfg.len_hi,
                          seed, nan_pad)
+
+
+def cu_seqlens(lengths) -> torch.Tensor:
+    """Offsets [0, L0, L0+L1, ...] (int32, B + 1 entries) of sequences packed end to end."""
+    out = [0]
+    for L in lengths:
+        out.append(out[-1] + int(L))
+    return torch.tensor(out, dtype=torch.int32)
+
+
+def varlen_inputs(lens_q, lens_k, Hq: int, Hkv: int, d: int, seed: int = 0,
+                  packed_qkv: bool = False):
+    """A packed variable-length batch on the CPU (bf16):
+    (cu_q, cu_k int32 [B+1], q [total_q, Hq, d], k and v [total_k, Hkv, d]).
+
+    Draw order: q, then k, then v, each fp32 ``randn`` in the packed layout.  With
+    ``packed_qkv`` (needs lens_q == lens_k) one [total, Hq + 2*Hkv, d] tensor is drawn
+    instead and q, k, v are views of its head ranges, the layout of a fused QKV
+    projection (their token stride is (Hq + 2*Hkv) * d).
+    """
+    cu_q, cu_k = cu_seqlens(lens_q), cu_seqlens(lens_k)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    g = torch.Generator("cpu").manual_seed(seed)
+    if packed_qkv:
+        if [int(x) for x in lens_q] != [int(x) for x in lens_k]:
+            raise ValueError("packed QKV needs equal query and key lengths")
+        qkv = torch.randn((tq, Hq + 2 * Hkv, d), generator=g, dtype=torch.float32)
+        qkv = qkv.to(torch.bfloat16)
+        return cu_q, cu_k, qkv[:, :Hq], qkv[:, Hq:Hq + Hkv], qkv[:, Hq + Hkv:]
+    q = torch.randn((tq, Hq, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((tk, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return cu_q, cu_k, q, k, v
+
+
+def varlen_inputs_for(cfg: VarlenConfig, seed: int = 0):
+    """(lengths int32 [B], cu_q, cu_k, q, k, v) of a VarlenConfig: lengths drawn with
+    ``decode_lengths`` from the same seed, then the packed tensors (seed + 1)."""
+    lengths = decode_lengths(cfg.B, cfg.len_lo, cfg.len_hi, seed=seed)
+    cu_q, cu_k, q, k, v = varlen_inputs(lengths, lengths, cfg.Hq, cfg.Hkv, cfg.d, seed=seed + 1)
+    return (lengths, cu_q, cu_k, q, k, v)
 
 
 def decode_bytes(lengths, Hq: int, Hkv: int, d: int) -> float:
