@@ -29,11 +29,16 @@
 //     (VALU) so the two can overlap.
 //   * Row chunks in LDS are XOR-swizzled so the MFMA operand reads are free of
 //     bank conflicts.
-//   * exp2 with scale*log2(e) folded into one FMA per score.  The running maximum
-//     used for the exponent is only moved when a block's maximum exceeds it by
-//     more than kTau (base-2 units): the online-softmax identity holds for any
-//     common reference value, and a bounded lag keeps exp2 <= 2^kTau, so most
-//     blocks skip the accumulator rescale entirely.
+//   * exp2 with scale*log2(e) folded into one FMA per score.  The exponent
+//     reference is the first block's row maximum, and it is moved (to a half
+//     block's row maximum, with the accumulator rescale) only when that half
+//     block's exponentials add up to more than kSumCap in some lane: the
+//     online-softmax identity holds for any common reference value, and the cap
+//     keeps every weight <= 2^8.  The common case therefore computes no row
+//     maximum and no rescale at all; the rare half block that trips the cap is
+//     recomputed after the move.
+//   * The softmax of each block is done in two 32-key halves: the first overlaps
+//     the next block's score MFMAs, the second the first half's P.V MFMAs.
 //   * Buffer loads clip at the end of each (batch, head) slice, so rows past Nq
 //     or Nk read as zeros without branches.
 //   * Workgroups are numbered so that each XCD (own L2) receives a contiguous slice
@@ -51,7 +56,7 @@ namespace fa {
 namespace {
 
 constexpr int kBN = 64;        // keys per K/V block
-constexpr float kTau = 8.f;    // largest lag of the exponent reference (base 2)
+constexpr float kSumCap = 256.f;  // largest per-lane half-block sum of exp2(S*c - m_ref)
 constexpr int kNumXcd = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -313,44 +318,43 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
       }
   };
 
-  // Block maximum of each row in base-2 units (c > 0).
-  auto row_max = [&](const f32x16* s) __attribute__((always_inline)) {
-    float mx = s[0][0];
+  // Maximum of each row over keys 32h .. 32h + 31 of the block, base-2 units (c > 0).
+  auto row_max = [&](const f32x16* s, int h) __attribute__((always_inline)) {
+    float mx = s[h][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[h][r]);
     return xor32_max(mx) * c;
   };
 
-  // Move the exponent reference when a row's block max exceeds it by more than kTau
-  // (online-softmax merge, [FA-notes] §4): old sums and accumulator scale by
-  // exp2(m_old - m_new).  Uniform branch across the wave; rare after the first blocks.
-  auto maybe_rescale = [&](float m_blk) __attribute__((always_inline)) {
-    if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
-      const float m_new = fmaxf(m_ref, m_blk);
-      // 0 on the first block; a row that has seen no visible key yet keeps alpha = 1
-      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_ref - m_new);
-      l_run *= alpha;
-      l_lse *= alpha;
+  // Move the exponent reference up to the block's row max (online-softmax merge,
+  // [FA-notes] §4): old sums and accumulator scale by exp2(m_old - m_new).
+  auto rescale_to = [&](float m_blk) __attribute__((always_inline)) {
+    const float m_new = fmaxf(m_ref, m_blk);
+    // a row that has seen no visible key yet keeps alpha = 1
+    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_ref - m_new);
+    l_run *= alpha;
+    l_lse *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      m_ref = m_new;
-    }
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    m_ref = m_new;
   };
 
-  // P = exp2(S*c - m_ref), its bf16 fragments, and both row sums.  O's normaliser
-  // adds up exactly the bf16-rounded weights (v_dot2 with (1, 1)), so O = acc / l is
-  // a true weighted mean of V whatever the reference; the LSE uses the unrounded sum.
-  auto exp_pack = [&](f32x16* s, bf16x8* pf) __attribute__((always_inline)) {
+  // P = exp2(S*c - m_ref) for keys 32h .. 32h + 31 of the block (score registers s[h],
+  // P fragments pf[2h], pf[2h + 1]) and this lane's two partial row sums over them: `ex`
+  // of the fp32 weights (for the LSE) and `rs` of the bf16-rounded ones (v_dot2 with
+  // (1, 1)); O's normaliser adds up exactly the rounded weights, so O = acc / l is a true
+  // weighted mean of V whatever the reference.
+  auto exp_pack = [&](f32x16* s, bf16x8* pf, int h, float& ex, float& rs)
+      __attribute__((always_inline)) {
     const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
     float ex0 = 0.f, ex1 = 0.f, rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-    for (int u = 0; u < kBN / 16; ++u) {
-      const int kb = u >> 1;
-      const int base = 8 * (u & 1);
+    for (int uu = 0; uu < 2; ++uu) {
+      const int u = 2 * h + uu;
+      const int kb = h;
+      const int base = 8 * uu;
       u32x4 w;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -364,16 +368,32 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
       }
       pf[u] = __builtin_bit_cast(bf16x8, w);
     }
-    l_lse += ex0 + ex1;
-    l_run += rs0 + rs1;
+    ex = ex0 + ex1;
+    rs = rs0 + rs1;
   };
 
-  // O^T += V^T P^T, V^T through transposed LDS reads.
-  auto pv = [&](const uint16_t* vt, const bf16x8* pf) __attribute__((always_inline)) {
+  // Fold one half block's weights into the running sums.  A lane whose half-block sum
+  // exceeds the cap (a score well above the reference, or a reference still at -inf)
+  // sends the wave through the rare path: reference moved to the half block's row max
+  // (the part of O already accumulated is rescaled with the sums), half block
+  // recomputed.  NaN sums take that path too and then propagate.
+  auto commit_half = [&](f32x16* s, bf16x8* pf, int h, float ex, float rs)
+      __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(!(ex <= kSumCap)) != 0) {
+      rescale_to(row_max(s, h));
+      exp_pack(s, pf, h, ex, rs);
+    }
+    l_lse += ex;
+    l_run += rs;
+  };
+
+  // O^T += V^T P^T over keys 32h .. 32h + 31 of the block, V^T through transposed LDS
+  // reads.
+  auto pv = [&](const uint16_t* vt, const bf16x8* pf, int h) __attribute__((always_inline)) {
     const __attribute__((address_space(3))) char* vb =
         (const __attribute__((address_space(3))) char*)(vt);
 #pragma unroll
-    for (int u = 0; u < kBN / 16; ++u)
+    for (int u = 2 * h; u < 2 * h + 2; ++u)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -398,14 +418,14 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   __syncthreads();
   qk(ks[0], s_a);
   if (need_mask(0)) mask(s_a, 0);
-  maybe_rescale(row_max(s_a));
+  m_ref = fmaxf(row_max(s_a, 0), row_max(s_a, 1));  // first reference (acc, sums still 0)
 
-  // ---- software pipeline.  Iteration j (scores of block j already masked, their max
-  // folded into the reference):
-  //   phase 1: MFMA S(j+1) = K(j+1) Q^T      | VALU exp2 / pack / sums of block j
+  // ---- software pipeline.  Iteration j (scores of block j already masked):
+  //   phase 1: MFMA S(j+1) = K(j+1) Q^T          | VALU softmax of keys 0..31 of block j
   //   (diagonal or ragged block j+1 only: mask)
-  //   phase 2: MFMA O^T += V(j)^T P(j)^T     | VALU row max of block j+1
-  //   then the (rare) reference move for block j+1.
+  //   phase 2: MFMA O^T += V(j)^T P(j)^T, keys 0..31 | VALU softmax of keys 32..63
+  //   phase 3: MFMA O^T += V(j)^T P(j)^T, keys 32..63
+  // with the rare reference move (half block redone) after either softmax half.
   // Each phase is one basic block, so the scheduler can interleave that phase's MFMA
   // with its VALU work (one wave issues its instructions in order).
   auto step_next = [&](auto stage_c, int j, f32x16* s_cur, f32x16* s_nxt)
@@ -418,23 +438,31 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     issue_block<D, WAVES>(rv, vvo, (uint32_t)(j + 1) * kBN * kv_row_bytes, vs[1 - sc], wave);
     bf16x8 pf[kBN / 16];
     qk(ks[1 - sc], s_nxt);
-    exp_pack(s_cur, pf);
+    float ex, rs;
+    exp_pack(s_cur, pf, 0, ex, rs);
     // Keep the exp/pack work in this block: without a use here the compiler would sink
     // it past the mask branch, next to its only consumer, and nothing would overlap.
     asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pf[0])), "v"(__builtin_bit_cast(u32x4, pf[1])),
-                 "v"(__builtin_bit_cast(u32x4, pf[2])), "v"(__builtin_bit_cast(u32x4, pf[3])));
+                 "v"(ex), "v"(rs));
     if (need_mask(j + 1)) mask(s_nxt, j + 1);
-    pv(vs[sc], pf);
-    const float m_blk = row_max(s_nxt);
-    maybe_rescale(m_blk);
+    commit_half(s_cur, pf, 0, ex, rs);
+    pv(vs[sc], pf, 0);
+    exp_pack(s_cur, pf, 1, ex, rs);
+    commit_half(s_cur, pf, 1, ex, rs);
+    pv(vs[sc], pf, 1);
   };
   auto step_last = [&](auto stage_c, f32x16* s_cur) __attribute__((always_inline)) {
     constexpr int sc = decltype(stage_c)::value;
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
     bf16x8 pf[kBN / 16];
-    exp_pack(s_cur, pf);
-    pv(vs[sc], pf);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float ex, rs;
+      exp_pack(s_cur, pf, h, ex, rs);
+      commit_half(s_cur, pf, h, ex, rs);
+      pv(vs[sc], pf, h);
+    }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
