@@ -7,7 +7,8 @@ nothing from the product: the two share no code.  The only module both sides
 use is ``workloads`` (seeded input generators, no attention arithmetic).
 
 What it computes is plain *standard* attention, the one that materialises the
-score matrix S and the probability matrix P, written from these pages:
+score matrix S and the probability matrix P (and its gradient, by the same
+materialised P), written from these pages:
 
   [FA-notes]   "flash-attn" notes, minjae-portfolio.vercel.app/notes/flash-attn
   [FA-evo]     "Attention is All You Need부터 FlashAttention-3까지: Transformer Attention
@@ -21,6 +22,7 @@ inputs, a library routine).  No function here is "parity unpinned".
 """
 from .attention import (  # noqa: F401
     attention,
+    attention_backward,
     attention_probs,
     attention_varlen,
     decode_attention,

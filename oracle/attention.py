@@ -219,6 +219,74 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
     return o, lse
 
 
+def attention_backward(q, k, v, do, scale: float, causal: bool,
+                       kv_heads: Optional[Sequence[int]] = None,
+                       rows: Optional[Tuple[int, int]] = None,
+                       keys: Optional[Tuple[int, int]] = None,
+                       row_block: Optional[int] = None):
+    """Gradients of standard attention: dQ, dK, dV for an upstream gradient dO.
+
+    [FA-notes] §5.2 sketches the backward pass: P is rebuilt from Q, K and the
+    forward's softmax statistics, then dV = P^T dO and dP = dO V^T, the remaining
+    steps being elided; [LLM-basics] ③-5 names the same recomputation for training.
+    The steps after dP are the derivative of the row softmax (the Jacobian of
+    p = softmax(s) is diag(p) - p p^T), written out per row i:
+        D_i   = sum_j P_ij dP_ij
+        dS_ij = P_ij (dP_ij - D_i)
+        dQ    = scale * dS K,    dK = scale * dS^T Q,    dV = P^T dO.
+    Here P is recomputed from scratch (the standard attention of ``attention``,
+    causal mask included), so this function needs no forward output.  GQA: the
+    dK and dV of a K/V head add up the contributions of its Hq/Hkv query heads.
+
+    q, do: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d].  Returns (dq [B, Nq, Hq, d],
+    dk, dv [B, Nk, Hkv, d]) in float64.  ``kv_heads`` restricts the work to some
+    K/V heads (and their query heads), ``rows`` the dQ rows returned, ``keys`` the
+    dK/dV keys returned (an empty key range skips dK/dV, and then only the rows
+    asked for are visited); entries not computed are NaN.  ``row_block`` bounds
+    memory by visiting that many query rows at a time (rows are independent, and
+    dK, dV are sums over rows).
+    """
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    group = Hq // Hkv
+    dq = torch.full((B, Nq, Hq, d), float("nan"), dtype=f64)
+    dk = torch.full((B, Nk, Hkv, d), float("nan"), dtype=f64)
+    dv = torch.full((B, Nk, Hkv, d), float("nan"), dtype=f64)
+    r0, r1 = rows if rows is not None else (0, Nq)
+    k0, k1 = keys if keys is not None else (0, Nk)
+    want_kv = k1 > k0
+    a0, a1 = (0, Nq) if want_kv else (r0, r1)
+    step = row_block or max(a1 - a0, 1)
+    for b in range(B):
+        for kvh in (kv_heads if kv_heads is not None else range(Hkv)):
+            kk = _as64(k[b, :, kvh, :])
+            vv = _as64(v[b, :, kvh, :])
+            dk_acc = torch.zeros((k1 - k0, d), dtype=f64)
+            dv_acc = torch.zeros((k1 - k0, d), dtype=f64)
+            for h in range(kvh * group, (kvh + 1) * group):
+                for a in range(a0, a1, step):
+                    e_ = min(a + step, a1)
+                    qq = _as64(q[b, a:e_, h, :])
+                    dd = _as64(do[b, a:e_, h, :])
+                    s = _scores(qq, kk, scale, a, Nq, causal)
+                    m = torch.amax(s, dim=1, keepdim=True)
+                    ex = torch.exp(s - m)
+                    p = ex / torch.sum(ex, dim=1, keepdim=True)        # P
+                    dp = dd @ vv.transpose(0, 1)                       # dP = dO V^T
+                    dsum = torch.sum(p * dp, dim=1, keepdim=True)      # D
+                    ds = p * (dp - dsum)                               # dS
+                    lo, hi = max(a, r0), min(e_, r1)
+                    if lo < hi:
+                        dq[b, lo:hi, h, :] = scale * (ds[lo - a:hi - a] @ kk)
+                    if want_kv:
+                        dv_acc += p[:, k0:k1].transpose(0, 1) @ dd
+                        dk_acc += scale * (ds[:, k0:k1].transpose(0, 1) @ qq)
+            if want_kv:
+                dk[b, k0:k1, kvh, :] = dk_acc
+                dv[b, k0:k1, kvh, :] = dv_acc
+    return dq, dk, dv
+
+
 def online_softmax_update(m_prev: torch.Tensor, l_prev: torch.Tensor, acc_prev: torch.Tensor,
                           s_block: torch.Tensor, v_block: torch.Tensor):
     """One block step of the online softmax, per row.

@@ -548,7 +548,147 @@ def pin_sdpa_crosscheck(orc):
         _close(lse, torch.logsumexp(s, dim=-1), 1e-12, "logsumexp LSE")
 
 
+def _sdpa_grads(q, k, v, do, scale, causal):
+    """Gradients of torch's fp64 CPU scaled_dot_product_attention through autograd (K/V
+    heads repeated for GQA, so autograd adds the group's contributions itself)."""
+    import torch.nn.functional as F
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    qq, kk, vv = (t.clone().requires_grad_(True) for t in (q, k, v))
+    qt = qq.permute(0, 2, 1, 3)
+    kt = torch.repeat_interleave(kk, Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+    vt = torch.repeat_interleave(vv, Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+    mask = None
+    if causal:
+        i = torch.arange(Nq).unsqueeze(1)
+        j = torch.arange(Nk).unsqueeze(0)
+        mask = j <= i + (Nk - Nq)
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    return torch.autograd.grad((o.permute(0, 2, 1, 3) * do).sum(), (qq, kk, vv))
+
+
+def pin_bwd_autograd(orc):
+    """The backward against autograd of a library routine (torch's SDPA, fp64 CPU):
+    MHA and GQA, causal with Nq == Nk and Nq < Nk (bottom-right), non-causal."""
+    for (B, Nq, Nk, Hq, Hkv, d, causal, sc) in ((1, 6, 6, 1, 1, 4, False, 0.5),
+                                                (2, 9, 9, 4, 2, 5, True, 0.4),
+                                                (1, 5, 11, 6, 2, 3, True, 0.9),
+                                                (1, 12, 7, 4, 1, 8, False, 0.35)):
+        q = _rand((B, Nq, Hq, d), 180)
+        k = _rand((B, Nk, Hkv, d), 181)
+        v = _rand((B, Nk, Hkv, d), 182)
+        do = _rand((B, Nq, Hq, d), 183)
+        dq, dk, dv = orc.attention_backward(q, k, v, do, sc, causal)
+        gq, gk, gv = _sdpa_grads(q, k, v, do, sc, causal)
+        _close(dq, gq, 1e-12, "bwd dQ vs autograd")
+        _close(dk, gk, 1e-12, "bwd dK vs autograd")
+        _close(dv, gv, 1e-12, "bwd dV vs autograd")
+
+
+def pin_bwd_finite_differences(orc):
+    """Brute force: central differences of L = sum(O * dO) through the (pinned) forward,
+    for every input entry of a tiny causal GQA case."""
+    B, Nq, Nk, Hq, Hkv, d, sc = 1, 3, 4, 2, 1, 2, 0.8
+    q = _rand((B, Nq, Hq, d), 190)
+    k = _rand((B, Nk, Hkv, d), 191)
+    v = _rand((B, Nk, Hkv, d), 192)
+    do = _rand((B, Nq, Hq, d), 193)
+    grads = orc.attention_backward(q, k, v, do, sc, True)
+
+    def loss(qq, kk, vv):
+        o, _ = orc.attention(qq, kk, vv, sc, True)
+        return float((o * do).sum())
+    h = 1e-5
+    for which, x in enumerate((q, k, v)):
+        for idx in range(x.numel()):
+            xp, xm = x.clone(), x.clone()
+            xp.view(-1)[idx] += h
+            xm.view(-1)[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grads[which].reshape(-1)[idx].item()) < 1e-8, (which, idx)
+
+
+def pin_bwd_closed_forms(orc):
+    """Closed forms.  K = 0 and every V row equal to c: every visible key has weight
+    1/n_i, O = c whatever the scores, so dQ = dK = 0 and dV_j = sum over the rows i that
+    see key j of dO_i / n_i.  A single key: P = 1, dQ = dK = 0, dV = sum_i dO_i."""
+    B, Nq, Nk, Hq, Hkv, d = 1, 5, 7, 2, 1, 3
+    q = _rand((B, Nq, Hq, d), 200)
+    k = torch.zeros((B, Nk, Hkv, d), dtype=f64)
+    c = _rand((d,), 201)
+    v = c.expand(B, Nk, Hkv, d).clone()
+    do = _rand((B, Nq, Hq, d), 202)
+    dq, dk, dv = orc.attention_backward(q, k, v, do, 0.7, True)
+    _close(dq, torch.zeros_like(dq), 1e-14, "K=0, const V: dQ")
+    _close(dk, torch.zeros_like(dk), 1e-14, "K=0, const V: dK")
+    want = torch.zeros((Nk, d), dtype=f64)
+    for h in range(Hq):
+        for i in range(Nq):
+            n = i + (Nk - Nq) + 1
+            want[:n] += do[0, i, h] / n
+    _close(dv[0, :, 0], want, 1e-13, "K=0: dV row means")
+    q1 = _rand((2, 4, 2, 3), 203)
+    k1 = _rand((2, 1, 2, 3), 204)
+    v1 = _rand((2, 1, 2, 3), 205)
+    do1 = _rand((2, 4, 2, 3), 206)
+    dq, dk, dv = orc.attention_backward(q1, k1, v1, do1, 1.3, False)
+    _close(dq, torch.zeros_like(dq), 1e-14, "one key: dQ")
+    _close(dk, torch.zeros_like(dk), 1e-14, "one key: dK")
+    _close(dv[:, 0], do1.sum(dim=1), 1e-13, "one key: dV")
+    # Scores hundreds apart ([LLM-basics] ③-1: exp of large scores overflows without the
+    # max shift): P is one-hot on each row's last visible key, so that key's dV is the sum
+    # of the dO rows it wins, every other dV row is 0, and dQ = dK = 0.
+    Nq, Nk = 3, 5
+    qb = torch.zeros((1, Nq, 1, 2), dtype=f64)
+    qb[..., 0] = 30.0
+    kb = torch.zeros((1, Nk, 1, 2), dtype=f64)
+    kb[0, :, 0, 0] = 30.0 * torch.arange(Nk, dtype=f64)
+    vb = _rand((1, Nk, 1, 2), 207)
+    dob = _rand((1, Nq, 1, 2), 208)
+    dq, dk, dv = orc.attention_backward(qb, kb, vb, dob, 1.0, True)
+    want = torch.zeros((Nk, 2), dtype=f64)
+    for i in range(Nq):
+        want[i + (Nk - Nq)] += dob[0, i, 0]
+    _close(dv[0, :, 0], want, 1e-14, "one-hot P: dV")
+    _close(dq, torch.zeros_like(dq), 1e-14, "one-hot P: dQ")
+    _close(dk, torch.zeros_like(dk), 1e-14, "one-hot P: dK")
+
+
+def pin_bwd_invariants(orc):
+    """Invariants of the softmax gradient: every row of dS sums to 0, so the dK rows of a
+    head add up to 0; and adding one vector w to every key adds Q_i.w to a whole score
+    row, which changes neither P nor (since rows of dS sum to 0) dQ, dK or dV."""
+    B, Nq, Nk, Hq, Hkv, d = 2, 6, 9, 4, 2, 5
+    q = _rand((B, Nq, Hq, d), 210)
+    k = _rand((B, Nk, Hkv, d), 211)
+    v = _rand((B, Nk, Hkv, d), 212)
+    do = _rand((B, Nq, Hq, d), 213)
+    w = _rand((d,), 214)
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_backward(q, k, v, do, 0.45, causal)
+        _close(dk.sum(dim=1), torch.zeros((B, Hkv, d), dtype=f64), 1e-13, "sum of dK rows")
+        dq2, dk2, dv2 = orc.attention_backward(q, k + w, v, do, 0.45, causal)
+        _close(dq2, dq, 1e-12, "key shift: dQ")
+        _close(dk2, dk, 1e-12, "key shift: dK")
+        _close(dv2, dv, 1e-12, "key shift: dV")
+        # restricted calls return the same numbers
+        rq, rk, rv = orc.attention_backward(q, k, v, do, 0.45, causal, kv_heads=[1], rows=(2, 5),
+                                            keys=(3, 8), row_block=4)
+        _close(rq[:, 2:5, 2:4], dq[:, 2:5, 2:4], 1e-13, "restricted dQ")
+        _close(rk[:, 3:8, 1], dk[:, 3:8, 1], 1e-13, "restricted dK")
+        _close(rv[:, 3:8, 1], dv[:, 3:8, 1], 1e-13, "restricted dV")
+        oq, _, _ = orc.attention_backward(q, k, v, do, 0.45, causal, rows=(1, 4), keys=(0, 0))
+        _close(oq[:, 1:4], dq[:, 1:4], 1e-13, "rows-only dQ")
+
+
 ALL_PINS = [
+    pin_bwd_autograd,
+    pin_bwd_finite_differences,
+    pin_bwd_closed_forms,
+    pin_bwd_invariants,
     pin_varlen_constant_v,
     pin_varlen_causal_alignment,
     pin_varlen_empty_sequences,

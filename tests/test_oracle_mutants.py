@@ -24,11 +24,12 @@ MUTANTS = {
     "gqa modulo": ("kvh = h // group", "kvh = h % Hkv"),
     "lse without ln l": ("(m + torch.log(l)).squeeze(1)", "m.squeeze(1)"),
     "wrong value operand": ("o[b, a:e_, h, :] = p @ vv", "o[b, a:e_, h, :] = p @ kk"),
-    "max over wrong axis": ("m = torch.amax(s, dim=1, keepdim=True)",
-                            "m = torch.amax(s, dim=0, keepdim=True)"),
+    "max over wrong axis": ("m = torch.amax(s, dim=1, keepdim=True)\n                ex = torch.exp(s - m)\n                l = ",
+                            "m = torch.amax(s, dim=0, keepdim=True)\n                ex = torch.exp(s - m)\n                l = "),
     "sum over wrong axis": ("l = torch.sum(ex, dim=1, keepdim=True)",
                             "l = torch.sum(ex, dim=0, keepdim=True)"),
-    "no max shift in attention": ("ex = torch.exp(s - m)", "ex = torch.exp(s)"),
+    "no max shift in attention": ("ex = torch.exp(s - m)\n                l = ", "ex = torch.exp(s)\n                l = "),
+    "bwd no max shift": ("ex = torch.exp(s - m)\n                    p = ", "ex = torch.exp(s)\n                    p = "),
     "softmax without max shift": ("e = torch.exp(x - m)", "e = torch.exp(x)"),
     "alpha sign": ("alpha = torch.exp(m_prev - m_new)", "alpha = torch.exp(m_new - m_prev)"),
     "beta dropped on acc": ("(beta.unsqueeze(-1) * p_cur) @", "(p_cur) @"),
@@ -48,6 +49,22 @@ MUTANTS = {
     "varlen key count from the query count": ("k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b + 1])",
                                               "k0, k1 = int(cu_seqlens_k[b]), int(cu_seqlens_k[b]) + (q1 - q0)"),
     "varlen keyless sequence not skipped": ("if q1 == q0 or k1 == k0:", "if q1 == q0:"),
+    "bwd drops the D term": ("ds = p * (dp - dsum)", "ds = p * dp"),
+    "bwd D over the wrong axis": ("dsum = torch.sum(p * dp, dim=1, keepdim=True)",
+                                  "dsum = torch.sum(p * dp, dim=0, keepdim=True)"),
+    "bwd dQ without scale": ("dq[b, lo:hi, h, :] = scale * (ds[lo - a:hi - a] @ kk)",
+                             "dq[b, lo:hi, h, :] = (ds[lo - a:hi - a] @ kk)"),
+    "bwd dQ from V": ("dq[b, lo:hi, h, :] = scale * (ds[lo - a:hi - a] @ kk)",
+                      "dq[b, lo:hi, h, :] = scale * (ds[lo - a:hi - a] @ vv)"),
+    "bwd dP from K": ("dp = dd @ vv.transpose(0, 1)", "dp = dd @ kk.transpose(0, 1)"),
+    "bwd dV from dS": ("dv_acc += p[:, k0:k1].transpose(0, 1) @ dd",
+                       "dv_acc += ds[:, k0:k1].transpose(0, 1) @ dd"),
+    "bwd dK from dO": ("dk_acc += scale * (ds[:, k0:k1].transpose(0, 1) @ qq)",
+                       "dk_acc += scale * (ds[:, k0:k1].transpose(0, 1) @ dd)"),
+    "bwd GQA keeps the last head only": ("dv_acc += p[:, k0:k1].transpose(0, 1) @ dd",
+                                          "dv_acc = p[:, k0:k1].transpose(0, 1) @ dd"),
+    "bwd unnormalised P": ("p = ex / torch.sum(ex, dim=1, keepdim=True)        # P",
+                           "p = ex        # P"),
     "paged ignores block table": ("page = int(block_table[b][j])", "page = j"),
     "paged reads whole last page": ("n = min(page_size, L - j * page_size)", "n = page_size"),
     "paged misses partial last page": ("for j in range((L + page_size - 1) // page_size):",
