@@ -9,9 +9,9 @@ One step = one pass of the whole hot path on resident synthetic inputs:
     the merge kernel.
 `value` is the prefill's algorithmic TFLOP/s (4*B*Hq*Nq*Nk*d / 2 for causal) over
 its measured kernel time; the decode's HBM GB/s (compulsory K/V/q/O/LSE bytes)
-is reported alongside, and so are the paged-KV decode and the packed variable-length
-prefill (16 causal GQA sequences, lengths ~U[512, 16384], one launch), each timed on
-its own after the step.  Kernel times come from HIP events recorded on the
+is reported alongside, and so are the paged-KV decode, the packed variable-length
+prefill (16 causal GQA sequences, lengths ~U[512, 16384], one launch) and the backward
+pass on the prefill workload's shape, each timed on its own after the step.  Kernel times come from HIP events recorded on the
 stream the kernels are launched on (torch's current stream), around every
 launch of the timed region.
 
@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length prefill measurement (reported beside "
                          "the step)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass measurement (reported beside the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -202,6 +204,51 @@ def bench_varlen(fa, W, dev, K):
             "kernel": "prefill_bf16_kernel<128, causal, varlen>"}
 
 
+def bench_backward(fa, W, pcfg, dev, K):
+    """fa_backward on the prefill workload's shape (seeded Q, K, V, dO; O and LSE from the
+    GPU forward, outside the timed region), timed on its own after the step.  Algorithmic
+    FLOP: the usual 2.5x the forward's (five products per visible pair: S, dP, dV, dK,
+    dQ); the kernels execute seven (S and dP are formed on both the dK/dV and the dQ
+    side), reported as executed_tflops."""
+    import torch
+    print(f"[bench] backward on {pcfg.name}", file=sys.stderr, flush=True)
+    q, k, v, do = W.backward_inputs(pcfg.B, pcfg.Hq, pcfg.Hkv, pcfg.Nq, pcfg.Nk, pcfg.d, seed=0,
+                                    qk_gain=pcfg.qk_gain)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    del q, k, v, do
+    o, lse = fa.fa_forward(qd, kd, vd, scale=pcfg.scale, causal=pcfg.causal)
+    dq = torch.empty_like(o)
+    dk = torch.empty(kd.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws = torch.empty((fa.fa_backward_workspace_bytes(pcfg.B, pcfg.Hq, pcfg.Nq),),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        fa.fa_backward(qd, kd, vd, o, lse, dod, scale=pcfg.scale, causal=pcfg.causal, dq=dq,
+                       dk=dk, dv=dv, workspace=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all().item(), "non-finite gradient"
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / K
+    flops = 2.5 * pcfg.flops()
+    tf = flops / (avg * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_call_ms": round(avg, 4),
+            "median_call_ms": round(sorted(ms)[K // 2], 4), "flop_per_call": flops,
+            "executed_tflops": round(tf * 7 / 5, 2), "workload": pcfg.workload,
+            "kernels": "prep (D, lse2) + dK/dV per 128 keys + dQ per 128 rows (one call)"}
+
+
 def cpu_baseline_decode(cfg, lengths, q, kc, vc, target_s):
     import torch
     import oracle
@@ -352,10 +399,14 @@ def main():
                             "traffic_merge": profiled_traffic("decode_merge_kernel<128>")}
     if dec and not args.no_paged:
         result["decode_paged"] = bench_paged(fa, W, dcfg, dec, dev, K)
-    if not args.no_varlen:
+    if not args.no_varlen or not args.no_backward:
         del qd, kd, vd, o, lse
         torch.cuda.empty_cache()
+    if not args.no_varlen:
         result["prefill_varlen"] = bench_varlen(fa, W, dev, K)
+        torch.cuda.empty_cache()
+    if not args.no_backward:
+        result["backward"] = bench_backward(fa, W, pcfg, dev, max(2, K // 4))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_prefill(pcfg, args.cpu_seconds)

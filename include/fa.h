@@ -65,7 +65,7 @@ typedef enum {
                               multiple of 64 */
   FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned (or a packed row
                               stride is not a multiple of 8 elements) */
-  FA_ERR_WORKSPACE = -5,   /* decode workspace missing or smaller than required */
+  FA_ERR_WORKSPACE = -5,   /* decode or backward workspace missing or smaller than required */
   FA_ERR_HIP = -6          /* the kernel launch failed (hipGetLastError) */
 } fa_status;
 
@@ -145,6 +145,44 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, float* o, flo
                       int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
                       float scale, int causal, int q_row_stride, int k_row_stride,
                       int v_row_stride, hipStream_t stream);
+
+/*
+ * fa_backward_workspace_bytes — bytes of device workspace fa_backward needs: two fp32
+ * vectors of B * Hq * Nq entries (D_i and LSE_i log2 e), each padded to 256 bytes.
+ * Returns 0 for non-positive sizes.
+ */
+size_t fa_backward_workspace_bytes(int B, int Hq, int Nq);
+
+/*
+ * fa_backward — gradients of the bf16 forward (fa_forward) for an upstream gradient dO.
+ *
+ * [FA-notes] §5.2 sketches the backward pass: the probabilities are rebuilt on chip from
+ * Q, K and the statistics the forward stored, instead of being kept, and dV = P^T dO,
+ * dP = dO V^T ([LLM-basics] ③-5 names the same recomputation for training).  The steps
+ * the sketch leaves out are the derivative of the row softmax: D_i = sum_j P_ij dP_ij
+ * (computed as sum_c dO_ic O_ic), dS = P (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ * P = exp(scale Q K^T - LSE) uses the forward's LSE directly.  GQA: the dK and dV of a
+ * K/V head add up its Hq / Hkv query heads.  Deterministic (no atomics): one kernel
+ * forms dK and dV per block of 128 keys, another dQ per block of 128 query rows, each
+ * recomputing the S and dP blocks it needs.
+ *
+ *   q, k, v     as in fa_forward (bf16)                          (read)
+ *   o, lse      fp32 O [B, Nq, Hq, d] and LSE [B, Hq, Nq] of the forward on the same
+ *               q, k, v, scale and causal flag                    (read)
+ *   dout        bf16 dO [B, Nq, Hq, d]                            (read)
+ *   dq          fp32 [B, Nq, Hq, d]                               (written; every element)
+ *   dk, dv      fp32 [B, Nk, Hkv, d]                              (written; every element)
+ *   workspace   at least fa_backward_workspace_bytes(B, Hq, Nq) bytes, 16-byte aligned,
+ *               caller-owned; contents on entry do not matter
+ * Sizes, alignment and the causal rule are those of fa_forward.  The three kernels run in
+ * order on `stream`.  Products are bf16 x bf16 with fp32 accumulation: P and dS are
+ * rounded to bf16 for the products that take them.  Returns FA_OK or a negative
+ * fa_status.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int Nq,
+                int Nk, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
 
 /*
  * fa_decode_splitkv_workspace_bytes — bytes of device workspace that

@@ -11,6 +11,9 @@ Functions (same names as the C entry points):
   fa_forward_f32(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None)
   fa_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                     scale=None, causal=False, o=None, lse=None, stream=None)
+  fa_backward_workspace_bytes(B, Hq, Nq)
+  fa_backward(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None,
+              workspace=None, stream=None)
   fa_decode_splitkv_workspace_bytes(B, Hq, Nk_max, d, chunk=256)
   fa_decode_splitkv(q, k_cache, v_cache, seqlens_k, scale=None, chunk=256, o=None,
                     lse=None, workspace=None, stream=None)
@@ -62,6 +65,11 @@ def lib() -> ctypes.CDLL:
     L.fa_forward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i,
                                     i, i, i, vp]
     L.fa_forward_varlen.restype = i
+    L.fa_backward_workspace_bytes.argtypes = [i, i, i]
+    L.fa_backward_workspace_bytes.restype = sz
+    L.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz,
+                              vp]
+    L.fa_backward.restype = i
     L.fa_decode_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
     L.fa_decode_splitkv_workspace_bytes.restype = sz
     L.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -192,6 +200,48 @@ def fa_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
     if st != FA_OK:
         raise FAError(st, "fa_forward_varlen")
     return o, lse
+
+
+def fa_backward_workspace_bytes(B: int, Hq: int, Nq: int) -> int:
+    return int(lib().fa_backward_workspace_bytes(B, Hq, Nq))
+
+
+def fa_backward(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool = False,
+                dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of fa_forward: bf16 q/dout [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]; the forward's
+    fp32 o [B,Nq,Hq,d] and lse [B,Hq,Nq] -> (dq fp32 [B,Nq,Hq,d], dk, dv fp32 [B,Nk,Hkv,d])."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check_tensor(t, n, torch.bfloat16, 4)
+    _check_tensor(o, "o", torch.float32, 4)
+    _check_tensor(lse, "lse", torch.float32, 3)
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk_ = k.shape
+    if (tuple(v.shape) != tuple(k.shape) or Bk != B or dk_ != d or tuple(o.shape) != tuple(q.shape)
+            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Nq)):
+        raise ValueError("backward shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dq is None:
+        dq = torch.empty((B, Nq, Hq, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, Nk, Hkv, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, Nk, Hkv, d), dtype=torch.float32, device=q.device)
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_tensor(t, n, torch.float32, 4)
+    if tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
+        raise ValueError("dq / dk / dv have the wrong shape")
+    need = fa_backward_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    st = lib().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                           _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                           1 if causal else 0, _ptr(workspace),
+                           int(workspace.numel() * workspace.element_size()), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_backward")
+    return dq, dk, dv
 
 
 def fa_decode_splitkv_workspace_bytes(B: int, Hq: int, Nk_max: int, d: int, chunk: int = 256) -> int:

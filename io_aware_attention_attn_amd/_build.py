@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_prefill_bf16.hip", "fa_prefill_f32.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.hip", "fa_prefill_bf16.hip", "fa_prefill_f32.hip", "fa_decode.hip",
+           "fa_backward.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

@@ -111,6 +111,31 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, float* o, flo
   return fa::launch_prefill_bf16(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_backward_workspace_bytes(int B, int Hq, int Nq) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0) return 0;
+  return 2 * fa::backward_vec_bytes(B, Hq, Nq);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                const void* dout, float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int Nq,
+                int Nk, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal);
+  if (st != FA_OK) return st;
+  if ((long long)B * Hkv * ((Nk + 127) / 128) > INT_MAX) return FA_ERR_SHAPE;
+  if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv)) return FA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, Hq, Nq))
+    return FA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return FA_ERR_ALIGN;
+  fa::BackwardArgs a{q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr,
+                     B, Hq, Hkv, Nq, Nk, d, scale, causal ? 1 : 0};
+  a.dsum = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    fa::backward_vec_bytes(B, Hq, Nq));
+  return fa::launch_backward(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int chunk) {
   if (check_decode_sizes(B, Hq, 1, Nk_max, d, chunk) != FA_OK) return 0;
   const int mp = max_pieces_of(Nk_max, chunk);
@@ -184,7 +209,7 @@ const char* fa_status_str(int status) {
                                     "and page size must be positive multiples of 64";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a tensor pointer is not 16-byte aligned (or a "
                               "packed row stride is not a multiple of 8 elements)";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: decode workspace missing or too small";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
     default: return "unknown fa_status";
   }

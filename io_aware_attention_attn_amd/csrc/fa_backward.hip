@@ -1,0 +1,551 @@
+// fa_backward.hip — attention backward pass for gfx950 (bf16 MFMA, fp32 softmax math).
+//
+// Sources: the backward sketch of the "flash-attn" notes, §5.2 (P rebuilt on chip from
+// Q, K and the forward's softmax statistics instead of being read back; dV = P^T dO,
+// dP = dO V^T), the recomputation note of "LLM 기초 — Attention부터 FlashAttention까지"
+// ③-5, and the derivative of the row softmax for the steps the sketch leaves out:
+//   D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic,  dS = P * (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// P = exp(scale S - LSE) comes straight from the stored log-sum-exp: no row max and no
+// normaliser are recomputed.
+//
+// Three kernels, in stream order, none of them with atomics (results are bitwise
+// reproducible):
+//   bwd_prep_kernel   D_i = sum_c dO_ic O_ic and lse2_i = LSE_i * log2(e), per (b, h, i).
+//   bwd_dkdv_kernel   one workgroup per 128 keys of one (batch, K/V head): K and V of
+//                     those keys stay in registers while the Q and dO tiles of every
+//                     query head of the GQA group stream through LDS; dK and dV
+//                     accumulate in registers and are written once.
+//   bwd_dq_kernel     one workgroup per 128 query rows of one (batch, query head): Q and
+//                     dO rows stay in registers while K and V tiles stream through LDS;
+//                     dQ accumulates in registers.
+// S and dP are therefore formed twice (once per output side), which trades 40% more
+// MFMA work for having no cross-workgroup reduction at all.
+//
+// MFMA layouts (v_mfma_f32_32x32x16_bf16, D = A B): the A operand of lane l is row l%32,
+// k = 8(l/32) .. +7; B is column l%32, the same k; D holds column l%32, rows
+// 8(r/4) + 4(l/32) + r%4 in register r.  Tiles in LDS are read both as rows (16-byte
+// reads) and transposed (ds_read_b64_tr_b16), so one XOR swizzle serves both.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kXcd = 8;   // workgroups dispatched round-robin over 8 XCDs
+constexpr int kTile = 64;  // rows per LDS tile (keys for dQ, query rows for dK/dV)
+
+typedef __attribute__((address_space(3))) void blds_void_t;
+typedef __bf16 bbf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bbf16x4 blds_bf16x4_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Work item i of T, renumbered so each XCD receives a contiguous range of items.
+__device__ __forceinline__ int bxcd_remap(int g, int T) {
+  const int q = T / kXcd, r = T % kXcd;
+  const int x = g % kXcd, i = g / kXcd;
+  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// XOR applied to the 16-byte chunk index of a tile row.  Row reads: 16 consecutive rows
+// at one logical chunk fall on 16 different bank groups.  Transposed reads: the 4
+// consecutive rows x 4 chunks one half-wave touches are all distinct.
+template <int D>
+__device__ __forceinline__ int bswz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                  : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+// One 64-row tile (all D columns) of a [rows, H, D] bf16 tensor straight into LDS:
+// each instruction fills 1 KB in lane order, the global chunk a lane fetches is the one
+// that belongs at its swizzled LDS position.
+template <int D>
+struct TileShape {
+  static constexpr int CH = D / 8;                  // 16-byte chunks per row
+  static constexpr int PER_WAVE = kTile * CH / 64 / 4;  // instructions per wave (4 waves)
+};
+
+template <int D>
+__device__ __forceinline__ void tile_offsets(uint32_t* off, uint32_t row_bytes, int wave,
+                                             int lane) {
+#pragma unroll
+  for (int i = 0; i < TileShape<D>::PER_WAVE; ++i) {
+    const int lin = (wave * TileShape<D>::PER_WAVE + i) * 64 + lane;
+    const int row = lin / TileShape<D>::CH;
+    const int pos = lin % TileShape<D>::CH;
+    off[i] = (uint32_t)row * row_bytes + (uint32_t)(pos ^ bswz<D>(row)) * 16u;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_issue(__amdgpu_buffer_rsrc_t rs, const uint32_t* off,
+                                           uint32_t soff, uint16_t* tile, int wave) {
+#pragma unroll
+  for (int i = 0; i < TileShape<D>::PER_WAVE; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (blds_void_t*)(tile + (wave * TileShape<D>::PER_WAVE + i) * 512), 16, off[i], soff,
+        0, 0);
+}
+
+// LDS byte offset of the 16-byte chunk (2*st + hi) of tile row `row` (row reads).
+template <int D>
+__device__ __forceinline__ uint32_t row_chunk(int row, int chunk) {
+  return (uint32_t)(row * D * 2 + ((chunk ^ bswz<D>(row)) * 16));
+}
+
+// Per-lane LDS byte offsets of the transposed reads that form an A operand X^T[32 d x 16
+// rows] from a row-major tile: in each 16-lane group, lane p points at row r0 + p/4 and
+// columns d0 + 4(p%4) .. +3, and the group receives X[r0 + i][d0 + p], i = 0..3.  Rows
+// 16u + 8e + 4hi + p/4; the swizzle does not depend on u, so toff[db][e] plus 16u rows.
+template <int D>
+__device__ __forceinline__ void tr_offsets(uint32_t (*toff)[2], int lane) {
+  const int p = lane & 15;
+  const int g = lane >> 4;
+  const int hi = (lane >> 5) & 1;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = 8 * e + 4 * hi + (p >> 2);
+      const int dcol = 32 * db + 16 * (g & 1) + 4 * (p & 3);
+      toff[db][e] = (uint32_t)(row * D * 2 + (((dcol >> 3) ^ bswz<D>(row)) * 16) + (dcol & 7) * 2);
+    }
+}
+
+// A operand X^T[32 d (block db) x 16 rows (step u)] from a tile through transposed reads.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, const uint32_t (*toff)[2],
+                                             int db, int u) {
+  const __attribute__((address_space(3))) char* base =
+      (const __attribute__((address_space(3))) char*)(tile);
+  const bbf16x4 lo =
+      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((blds_bf16x4_t*)(base + toff[db][0] + 16 * u * D * 2));
+  const bbf16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((blds_bf16x4_t*)(base + toff[db][1] + 16 * u * D * 2));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------------------------------------
+// D_i = sum_c dO_ic O_ic and lse2_i = LSE_i log2(e).  D/8 lanes per row, 8 columns each.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ O,
+                                                       const uint16_t* __restrict__ dO,
+                                                       const float* __restrict__ LSE,
+                                                       float* __restrict__ Dws,
+                                                       float* __restrict__ L2ws, int B, int Hq,
+                                                       int Nq) {
+  constexpr int LPR = D / 8;
+  const long long rows = (long long)B * Nq * Hq;
+  const long long r = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (r < rows) {
+    const float* o = O + r * D + part * 8;
+    const u32x4 w = ldg128(dO + r * D + part * 8);
+    const f32x4 o0 = *reinterpret_cast<const f32x4*>(o);
+    const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc = fmaf(__uint_as_float(w[t] << 16), (t < 2 ? o0[2 * t] : o1[2 * t - 4]), acc);
+      acc = fmaf(__uint_as_float(w[t] & 0xffff0000u), (t < 2 ? o0[2 * t + 1] : o1[2 * t - 3]),
+                 acc);
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (r < rows && part == 0) {
+    const int h = (int)(r % Hq);
+    const long long bi = r / Hq;
+    const int i = (int)(bi % Nq);
+    const int b = (int)(bi / Nq);
+    const size_t idx = ((size_t)b * Hq + h) * Nq + i;
+    Dws[idx] = acc;
+    L2ws[idx] = LSE[idx] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dK, dV for 128 keys (32 per wave) of one (batch, K/V head).
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(1, 1))) void
+bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                const float* __restrict__ Dws, const float* __restrict__ L2ws,
+                float* __restrict__ dK, float* __restrict__ dV, int B, int Hq, int Hkv, int Nq,
+                int Nk, float c, float scale, int n_kblocks) {
+  constexpr int PW = TileShape<D>::PER_WAVE;
+  __shared__ __attribute__((aligned(1024))) uint16_t qs0[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t qs1[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t os0[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t os1[kTile * D];
+  __shared__ __attribute__((aligned(16))) float ls[2][2][kTile];  // [stage][lse2, D][row]
+  // stage buffers picked with a select (a runtime-indexed array of LDS pointers would
+  // need a static initializer the target cannot express)
+  auto qs = [&](int st) __attribute__((always_inline)) { return st ? qs1 : qs0; };
+  auto os = [&](int st) __attribute__((always_inline)) { return st ? os1 : os0; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int G = Hq / Hkv;
+  const int T = n_kblocks * B * Hkv;
+  const int lam = bxcd_remap((int)blockIdx.x, T);
+  const int kblk = lam % n_kblocks;  // heaviest (seen by the most query rows) first
+  const int bk = lam / n_kblocks;
+  const int kvh = bk % Hkv;
+  const int b = bk / Hkv;
+  const int n0 = kblk * 128;
+  const int key = n0 + wave * 32 + l32;  // this lane's key (column of S, dP, P, dS)
+  const int diag = Nk - Nq;              // key j visible from row i iff j <= i + diag
+
+  const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
+  const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
+
+  // K^T and V^T fragments of this lane's key (B operands; zeros past Nk)
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const __amdgpu_buffer_rsrc_t rk =
+        brsrc(K + ((size_t)b * Nk * Hkv + kvh) * D, (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
+    const __amdgpu_buffer_rsrc_t rv =
+        brsrc(V + ((size_t)b * Nk * Hkv + kvh) * D, (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const uint32_t off = (uint32_t)key * kv_row_bytes + (uint32_t)(16 * st + 8 * hi) * 2;
+      kf[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      vf[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+  }
+
+  // query tiles that can see any of the 128 keys: rows >= n0 - diag under the causal mask
+  const int m_first = CAUSAL ? max(0, n0 - diag) / kTile : 0;
+  const int n_mt = (Nq + kTile - 1) / kTile;
+  const int per_head = max(n_mt - m_first, 0);
+  const int n_it = per_head * G;
+
+  f32x16 dkt[D / 32], dvt[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dkt[i] = f32x16{};
+    dvt[i] = f32x16{};
+  }
+
+  uint32_t toff[D / 32][2];
+  tr_offsets<D>(toff, lane);
+  uint32_t tl[PW];
+  tile_offsets<D>(tl, q_row_bytes, wave, lane);
+
+  // iteration t -> (query head, query tile); LDS-DMA of its Q, dO, lse2 and D rows
+  auto issue = [&](int t, int stage) __attribute__((always_inline)) {
+    const int hq = kvh * G + t / per_head;
+    const int m = (m_first + t % per_head) * kTile;
+    const __amdgpu_buffer_rsrc_t rq =
+        brsrc(Q + ((size_t)b * Nq * Hq + hq) * D, (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
+    const __amdgpu_buffer_rsrc_t ro =
+        brsrc(dO + ((size_t)b * Nq * Hq + hq) * D, (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
+    tile_issue<D>(rq, tl, (uint32_t)m * q_row_bytes, qs(stage), wave);
+    tile_issue<D>(ro, tl, (uint32_t)m * q_row_bytes, os(stage), wave);
+    if (wave < 2) {
+      // rows past Nq read as 0: lse2 = 0 and D = 0 there, and Q, dO rows are 0 too, so
+      // those rows add nothing to dK or dV
+      const float* src = (wave == 0 ? L2ws : Dws) + ((size_t)b * Hq + hq) * Nq;
+      const __amdgpu_buffer_rsrc_t rl = brsrc(src, (uint32_t)Nq * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (blds_void_t*)(&ls[stage][wave][0]), 4,
+                                               (uint32_t)lane * 4, (uint32_t)m * 4, 0, 0);
+    }
+  };
+
+  if (n_it > 0) issue(0, 0);
+  for (int t = 0; t < n_it; ++t) {
+    const int st = t & 1;
+    const int m = (m_first + t % per_head) * kTile;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's part of tile t has landed
+    __syncthreads();                      // ... everyone's; stage st^1 is free again
+    if (t + 1 < n_it) issue(t + 1, st ^ 1);
+    const char* qt = reinterpret_cast<const char*>(qs(st));
+    const char* ot = reinterpret_cast<const char*>(os(st));
+
+    // S = Q K^T and dP = dO V^T for both 32-row halves (4 independent accumulators)
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh) {
+      s[rh] = f32x16{};
+      dp[rh] = f32x16{};
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {
+        const int row = 32 * rh + l32;
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + row_chunk<D>(row, 2 * kk + hi));
+        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(ot + row_chunk<D>(row, 2 * kk + hi));
+        s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], s[rh], 0, 0, 0);
+        dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], dp[rh], 0, 0, 0);
+      }
+
+    // P = exp2(S c - lse2_row) (0 where the key is not visible), dS = P (dP - D_row);
+    // both packed to bf16 as B operands (k = rows in the register order of D)
+    const int kmin = key - diag - m;  // causal: tile row r sees this key iff r >= kmin
+    u32x4 pw[4], dw[4];
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = 32 * rh + 8 * q4 + 4 * hi;  // tile rows r0 .. r0+3 of registers 4q4..
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&ls[st][0][r0]);
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(&ls[st][1][r0]);
+        float pv[4], dv4[4];
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          float p = fast_exp2(fmaf(s[rh][4 * q4 + t4], c, -l2[t4]));
+          if (CAUSAL) p = (r0 + t4 >= kmin) ? p : 0.f;
+          pv[t4] = p;
+          dv4[t4] = p * (dp[rh][4 * q4 + t4] - dd[t4]);
+        }
+        // registers 4q4 .. 4q4+3 are words 2(q4&1), +1 of B operand u (16-row step)
+        const int u = 2 * rh + (q4 >> 1);
+        const int w = 2 * (q4 & 1);
+        pw[u][w] = pack_bf16x2(pv[0], pv[1]);
+        pw[u][w + 1] = pack_bf16x2(pv[2], pv[3]);
+        dw[u][w] = pack_bf16x2(dv4[0], dv4[1]);
+        dw[u][w + 1] = pack_bf16x2(dv4[2], dv4[3]);
+      }
+    }
+    bf16x8 pp[4], dsp[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pp[u] = __builtin_bit_cast(bf16x8, pw[u]);
+      dsp[u] = __builtin_bit_cast(bf16x8, dw[u]);
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 rows (4 steps of 16)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 ao = tr_operand<D>(os(st), toff, db, u);
+        const bf16x8 aq = tr_operand<D>(qs(st), toff, db, u);
+        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pp[u], dvt[db], 0, 0, 0);
+        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsp[u], dkt[db], 0, 0, 0);
+      }
+    (void)m;
+  }
+
+  // dK = scale * (Q^T dS)^T, dV = (dO^T P)^T; lane = key, registers hold 4 consecutive d
+  if (key < Nk) {
+    float* krow = dK + (((size_t)b * Nk + key) * Hkv + kvh) * D;
+    float* vrow = dV + (((size_t)b * Nk + key) * Hkv + kvh) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * hi;
+        *reinterpret_cast<f32x4*>(krow + col) =
+            f32x4{dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale,
+                  dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(vrow + col) =
+            f32x4{dvt[db][4 * g], dvt[db][4 * g + 1], dvt[db][4 * g + 2], dvt[db][4 * g + 3]};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dQ for 128 query rows (32 per wave) of one (batch, query head).
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(1, 1))) void
+bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+              const float* __restrict__ Dws, const float* __restrict__ L2ws,
+              float* __restrict__ dQ, int B, int Hq, int Hkv, int Nq, int Nk, float c,
+              float scale, int n_mblocks) {
+  constexpr int PW = TileShape<D>::PER_WAVE;
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks1[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs1[kTile * D];
+  auto ks = [&](int st) __attribute__((always_inline)) { return st ? ks1 : ks0; };
+  auto vs = [&](int st) __attribute__((always_inline)) { return st ? vs1 : vs0; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // work order as in the forward: (batch, K/V head) major, heaviest query block first,
+  // the group's query heads adjacent
+  const int G = Hq / Hkv;
+  const int T = n_mblocks * B * Hq;
+  const int lam = bxcd_remap((int)blockIdx.x, T);
+  const int hg = lam % G;
+  const int rest = lam / G;
+  const int mb = n_mblocks - 1 - rest % n_mblocks;
+  const int bk = rest / n_mblocks;
+  const int kvh = bk % Hkv;
+  const int b = bk / Hkv;
+  const int hq = kvh * G + hg;
+  const int m0 = mb * 128;
+  const int qrow = m0 + wave * 32 + l32;  // this lane's query row (column of S^T, dP^T)
+  const int diag = Nk - Nq;
+
+  const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
+  const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
+
+  // Q and dO rows of this lane (B operands; zeros past Nq), and its lse2 / D
+  bf16x8 qf[D / 16], of[D / 16];
+  float l2 = 0.f, dd = 0.f;
+  {
+    const __amdgpu_buffer_rsrc_t rq =
+        brsrc(Q + ((size_t)b * Nq * Hq + hq) * D, (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
+    const __amdgpu_buffer_rsrc_t ro =
+        brsrc(dO + ((size_t)b * Nq * Hq + hq) * D, (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const uint32_t off = (uint32_t)qrow * q_row_bytes + (uint32_t)(16 * st + 8 * hi) * 2;
+      qf[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      of[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
+    }
+    if (qrow < Nq) {
+      const size_t idx = ((size_t)b * Hq + hq) * Nq + qrow;
+      l2 = L2ws[idx];
+      dd = Dws[idx];
+    }
+  }
+
+  int kend = Nk;
+  if (CAUSAL) kend = min(Nk, min(m0 + 128, Nq) - 1 + diag + 1);
+  const int n = (kend + kTile - 1) / kTile;
+
+  const __amdgpu_buffer_rsrc_t rk =
+      brsrc(K + ((size_t)b * Nk * Hkv + kvh) * D, (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
+  const __amdgpu_buffer_rsrc_t rv =
+      brsrc(V + ((size_t)b * Nk * Hkv + kvh) * D, (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
+  uint32_t tl[PW];
+  tile_offsets<D>(tl, kv_row_bytes, wave, lane);
+  uint32_t toff[D / 32][2];
+  tr_offsets<D>(toff, lane);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+
+  if (n > 0) {
+    tile_issue<D>(rk, tl, 0, ks(0), wave);
+    tile_issue<D>(rv, tl, 0, vs(0), wave);
+  }
+  for (int j = 0; j < n; ++j) {
+    const int st = j & 1;
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    if (j + 1 < n) {
+      tile_issue<D>(rk, tl, (uint32_t)(j + 1) * kTile * kv_row_bytes, ks(st ^ 1), wave);
+      tile_issue<D>(rv, tl, (uint32_t)(j + 1) * kTile * kv_row_bytes, vs(st ^ 1), wave);
+    }
+    const char* kt = reinterpret_cast<const char*>(ks(st));
+    const char* vt = reinterpret_cast<const char*>(vs(st));
+
+    // S^T = K Q^T and dP^T = V dO^T: keys 32kb + (register order), lane = query row
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 32 * kb + l32;
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt + row_chunk<D>(row, 2 * kk + hi));
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + row_chunk<D>(row, 2 * kk + hi));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], dp[kb], 0, 0, 0);
+      }
+
+    // dS^T = P^T (dP^T - D) with P^T = exp2(S^T c - lse2); keys past the end or (causal)
+    // past this row's last visible key get P = 0
+    const int lim = CAUSAL ? min(qrow + diag, Nk - 1) - j * kTile - 4 * hi
+                           : Nk - 1 - j * kTile - 4 * hi;
+    bf16x8 dsp[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kb = u >> 1;
+      const int base = 8 * (u & 1);
+      u32x4 w;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float v2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = base + 2 * t + e;
+          const int kl = kb * 32 + 8 * (r >> 2) + (r & 3);
+          float p = fast_exp2(fmaf(s[kb][r], c, -l2));
+          p = (kl <= lim) ? p : 0.f;
+          v2[e] = p * (dp[kb][r] - dd);
+        }
+        w[t] = pack_bf16x2(v2[0], v2[1]);
+      }
+      dsp[u] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    // dQ^T += K^T dS^T, K^T through transposed reads of the K tile
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 a = tr_operand<D>(ks(st), toff, db, u);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsp[u], acc[db], 0, 0, 0);
+      }
+  }
+
+  if (qrow < Nq) {
+    float* row = dQ + (((size_t)b * Nq + qrow) * Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(row + 32 * db + 8 * g + 4 * hi) =
+            f32x4{acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale, acc[db][4 * g + 2] * scale,
+                  acc[db][4 * g + 3] * scale};
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BackwardArgs& a, hipStream_t s) {
+  const long long rows = (long long)a.B * a.Nq * a.Hq;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                     0, s, a.o, static_cast<const uint16_t*>(a.dout), a.lse, a.dsum, a.lse2,
+                     a.B, a.Hq, a.Nq);
+  const float c = a.scale * kLog2e;
+  const int n_kblocks = (a.Nk + 127) / 128;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_kblocks * a.B * a.Hkv)),
+                     dim3(256), 0, s, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                     static_cast<const uint16_t*>(a.dout), a.dsum, a.lse2, a.dk, a.dv, a.B, a.Hq,
+                     a.Hkv, a.Nq, a.Nk, c, a.scale, n_kblocks);
+  const int n_mblocks = (a.Nq + 127) / 128;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_mblocks * a.B * a.Hq)),
+                     dim3(256), 0, s, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                     static_cast<const uint16_t*>(a.dout), a.dsum, a.lse2, a.dq, a.B, a.Hq,
+                     a.Hkv, a.Nq, a.Nk, c, a.scale, n_mblocks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
+  return a.causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
+}
+
+}  // namespace fa

@@ -46,6 +46,32 @@ struct DecodeArgs {
   int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
+// Backward: q, dout [B,Nq,Hq,d] bf16, k, v [B,Nk,Hkv,d] bf16, o [B,Nq,Hq,d] fp32 and
+// lse [B,Hq,Nq] fp32 from the forward; dq [B,Nq,Hq,d], dk, dv [B,Nk,Hkv,d] fp32.
+// Workspace: dsum = D_i and lse2 = LSE_i log2(e), each [B,Hq,Nq] fp32.
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* o;
+  const float* lse;
+  const void* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dsum;
+  float* lse2;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+};
+
+inline size_t backward_vec_bytes(int B, int Hq, int Nq) {
+  size_t n = (size_t)B * Hq * Nq * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t s);

@@ -242,7 +242,9 @@ def attention_backward(q, k, v, do, scale: float, causal: bool,
     dk, dv [B, Nk, Hkv, d]) in float64.  ``kv_heads`` restricts the work to some
     K/V heads (and their query heads), ``rows`` the dQ rows returned, ``keys`` the
     dK/dV keys returned (an empty key range skips dK/dV, and then only the rows
-    asked for are visited); entries not computed are NaN.  ``row_block`` bounds
+    asked for are visited; an empty row range skips dQ, and under the causal mask the
+    rows that cannot see the keys asked for are then skipped); entries not computed
+    are NaN.  ``row_block`` bounds
     memory by visiting that many query rows at a time (rows are independent, and
     dK, dV are sums over rows).
     """
@@ -256,6 +258,10 @@ def attention_backward(q, k, v, do, scale: float, causal: bool,
     k0, k1 = keys if keys is not None else (0, Nk)
     want_kv = k1 > k0
     a0, a1 = (0, Nq) if want_kv else (r0, r1)
+    if want_kv and causal and r1 <= r0:
+        # no dQ asked for: rows before k0 - (Nk - Nq) see none of the keys asked for (their
+        # P and dS columns there are exactly 0), so they add nothing to dK and dV
+        a0 = min(max(0, k0 - (Nk - Nq)), Nq)
     step = row_block or max(a1 - a0, 1)
     for b in range(B):
         for kvh in (kv_heads if kv_heads is not None else range(Hkv)):

@@ -682,6 +682,9 @@ def pin_bwd_invariants(orc):
         _close(rv[:, 3:8, 1], dv[:, 3:8, 1], 1e-13, "restricted dV")
         oq, _, _ = orc.attention_backward(q, k, v, do, 0.45, causal, rows=(1, 4), keys=(0, 0))
         _close(oq[:, 1:4], dq[:, 1:4], 1e-13, "rows-only dQ")
+        _, ok_, ov = orc.attention_backward(q, k, v, do, 0.45, causal, rows=(0, 0), keys=(6, 9))
+        _close(ok_[:, 6:9], dk[:, 6:9], 1e-13, "keys-only dK")
+        _close(ov[:, 6:9], dv[:, 6:9], 1e-13, "keys-only dV")
 
 
 ALL_PINS = [

@@ -36,6 +36,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(names) == {"fa_forward", "fa_forward_f32", "fa_forward_varlen",
+                          "fa_backward_workspace_bytes", "fa_backward",
                           "fa_decode_splitkv_workspace_bytes",
                           "fa_decode_splitkv", "fa_decode_paged", "fa_status_str"}
     for n in names:
@@ -118,6 +119,39 @@ def _varlen(L, q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, B=2, Hq=4, Hkv=2, max_q=64
 ])
 def test_varlen_rejects(L, kw, status):
     assert _varlen(L, **kw) == status
+
+
+def _bwd(L, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=64, Nk=64,
+         d=128, scale=0.1, causal=1, ws=P, ws_bytes=1 << 20):
+    return L.fa_backward(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                         ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(o=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(do=None), fa.FA_ERR_NULL),
+    (dict(dq=None), fa.FA_ERR_NULL),
+    (dict(dk=None), fa.FA_ERR_NULL),
+    (dict(dv=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
+    (dict(Nq=65, Nk=64), fa.FA_ERR_SHAPE),      # causal with more queries than keys
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(do=MIS), fa.FA_ERR_ALIGN),
+    (dict(dk=MIS), fa.FA_ERR_ALIGN),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), fa.FA_ERR_WORKSPACE),
+    (dict(ws=MIS), fa.FA_ERR_ALIGN),
+])
+def test_backward_rejects(L, kw, status):
+    assert _bwd(L, **kw) == status
+
+
+def test_backward_workspace_bytes(L):
+    assert fa.fa_backward_workspace_bytes(2, 3, 100) == 2 * ((2 * 3 * 100 * 4 + 255) // 256) * 256
+    assert fa.fa_backward_workspace_bytes(0, 3, 100) == 0
 
 
 def test_workspace_bytes(L):

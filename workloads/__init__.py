@@ -144,6 +144,21 @@ def prefill_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, dtype: s
     return _round(q, dtype), _round(k, dtype), _round(v, dtype)
 
 
+def backward_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int = 0,
+                    qk_gain: float = 1.0):
+    """bf16 Q, K, V as ``prefill_inputs`` (same draws), then the upstream gradient dO
+    [B,Nq,Hq,d] drawn next from the same generator as fp32 ``randn`` rounded to bf16."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((B, Nq, Hq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32)
+    do = torch.randn((B, Nq, Hq, d), generator=g, dtype=torch.float32)
+    if qk_gain != 1.0:
+        q.mul_(qk_gain)
+        k.mul_(qk_gain)
+    return tuple(t.to(torch.bfloat16) for t in (q, k, v, do))
+
+
 def prefill_inputs_for(cfg: PrefillConfig, seed: int = 0):
     return prefill_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.dtype, seed,
                           cfg.qk_gain)
