@@ -10,8 +10,9 @@ One step = one pass of the whole hot path on resident synthetic inputs:
 `value` is the prefill's algorithmic TFLOP/s (4*B*Hq*Nq*Nk*d / 2 for causal) over
 its measured kernel time; the decode's HBM GB/s (compulsory K/V/q/O/LSE bytes)
 is reported alongside, and so are the paged-KV decode, the packed variable-length
-prefill (16 causal GQA sequences, lengths ~U[512, 16384], one launch) and the backward
-pass on the prefill workload's shape, each timed on its own after the step.  Kernel times come from HIP events recorded on the
+prefill (16 causal GQA sequences, lengths ~U[512, 16384], one launch), the FP8 forward
+and the backward pass on the prefill workload's shape, each timed on its own after the
+step.  Kernel times come from HIP events recorded on the
 stream the kernels are launched on (torch's current stream), around every
 launch of the timed region.
 
@@ -33,6 +34,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA (twice the bf16 rate)
 
 
 def parse():
@@ -48,6 +50,8 @@ def parse():
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length prefill measurement (reported beside "
                          "the step)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 forward measurement (reported beside the step)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement (reported beside the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -202,6 +206,42 @@ def bench_varlen(fa, W, dev, K):
             "median_launch_ms": round(sorted(ms)[K // 2], 4), "flop_per_launch": flops,
             "workload": cfg.workload, "total_tokens": tq, "max_seqlen": max_q,
             "kernel": "prefill_bf16_kernel<128, causal, varlen>"}
+
+
+def bench_fp8(fa, W, pcfg, dev, K):
+    """fa_forward_fp8 on the prefill workload's shape (E4M3 codes of the same seeded draws,
+    per-tensor descales), timed on its own after the step; FLOP as the bf16 prefill."""
+    import torch
+    print(f"[bench] fp8 forward on {pcfg.name}", file=sys.stderr, flush=True)
+    q8, k8, v8, qd, kd, vd = W.fp8_inputs(pcfg.B, pcfg.Hq, pcfg.Hkv, pcfg.Nq, pcfg.Nk, pcfg.d,
+                                          seed=0, qk_gain=pcfg.qk_gain)
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    o = torch.empty((pcfg.B, pcfg.Nq, pcfg.Hq, pcfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((pcfg.B, pcfg.Hq, pcfg.Nq), dtype=torch.float32, device=dev)
+
+    def call():
+        fa.fa_forward_fp8(q8, k8, v8, qd, kd, vd, scale=pcfg.scale, causal=pcfg.causal, o=o,
+                          lse=lse)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / K
+    flops = pcfg.flops()
+    tf = flops / (avg * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_FP8_TFLOPS,
+            "frac": round(tf / PEAK_FP8_TFLOPS, 4), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "avg_launch_ms": round(avg, 4), "median_launch_ms": round(sorted(ms)[K // 2], 4),
+            "flop_per_launch": flops, "workload": pcfg.workload + " as E4M3 codes",
+            "kernel": "prefill_fp8_kernel<128, causal>"}
 
 
 def bench_backward(fa, W, pcfg, dev, K):
@@ -399,11 +439,14 @@ def main():
                             "traffic_merge": profiled_traffic("decode_merge_kernel<128>")}
     if dec and not args.no_paged:
         result["decode_paged"] = bench_paged(fa, W, dcfg, dec, dev, K)
-    if not args.no_varlen or not args.no_backward:
+    if not args.no_varlen or not args.no_backward or not args.no_fp8:
         del qd, kd, vd, o, lse
         torch.cuda.empty_cache()
     if not args.no_varlen:
         result["prefill_varlen"] = bench_varlen(fa, W, dev, K)
+        torch.cuda.empty_cache()
+    if not args.no_fp8:
+        result["prefill_fp8"] = bench_fp8(fa, W, pcfg, dev, K)
         torch.cuda.empty_cache()
     if not args.no_backward:
         result["backward"] = bench_backward(fa, W, pcfg, dev, max(2, K // 4))

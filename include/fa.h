@@ -105,6 +105,25 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
                    hipStream_t stream);
 
 /*
+ * fa_forward_fp8 — fa_forward with FP8 Q, K, V ([FA3-entry] §3 names FP8 low precision
+ * for the forward pass).
+ *
+ *   q            OCP FP8 E4M3 codes [B, Nq, Hq, d]      (read; value = code * q_descale)
+ *   k, v         OCP FP8 E4M3 codes [B, Nk, Hkv, d]     (read; value = code * k/v_descale)
+ *   o, lse       fp32 as in fa_forward                  (written)
+ *   q_descale, k_descale, v_descale   per-tensor positive finite factors
+ * Both products take E4M3 operands with fp32 accumulation: S = scale * q_descale *
+ * k_descale * (codes product); the weights P = exp(S - m) are rounded to E4M3 (round to
+ * nearest even; every weight is <= 2^8 by construction) for P V, O is normalised by the
+ * sum of those rounded weights and scaled by v_descale, and the LSE uses the fp32 sum of
+ * the unrounded weights.  Same sizes, alignment and causal rule as fa_forward;
+ * FA_ERR_SHAPE also for a descale that is not a positive finite number.
+ */
+int fa_forward_fp8(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   float q_descale, float k_descale, float v_descale, hipStream_t stream);
+
+/*
  * fa_forward_varlen — fa_forward over a batch of variable-length sequences packed
  * along the token axis, bf16 inputs.
  *

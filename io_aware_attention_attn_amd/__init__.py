@@ -9,6 +9,8 @@ of the computation runs in the library's HIP kernels; there is no fallback path.
 Functions (same names as the C entry points):
   fa_forward(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None)
   fa_forward_f32(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None)
+  fa_forward_fp8(q8, k8, v8, q_descale, k_descale, v_descale, scale=None, causal=False, o=None,
+                 lse=None, stream=None)
   fa_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                     scale=None, causal=False, o=None, lse=None, stream=None)
   fa_backward_workspace_bytes(B, Hq, Nq)
@@ -62,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.fa_forward.restype = i
     L.fa_forward_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     L.fa_forward_f32.restype = i
+    L.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, vp]
+    L.fa_forward_fp8.restype = i
     L.fa_forward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i,
                                     i, i, i, vp]
     L.fa_forward_varlen.restype = i
@@ -149,6 +153,36 @@ def fa_forward_f32(q, k, v, scale: Optional[float] = None, causal: bool = False,
     """fp32 variant of fa_forward (no 16-bit rounding anywhere)."""
     import torch
     return _forward(lib().fa_forward_f32, q, k, v, scale, causal, o, lse, stream, torch.float32)
+
+
+def fa_forward_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
+                   scale: Optional[float] = None, causal: bool = False, o=None, lse=None,
+                   stream=None):
+    """torch.float8_e4m3fn q8 [B,Nq,Hq,d], k8/v8 [B,Nk,Hkv,d] with per-tensor descales
+    (value = code * descale) -> (O fp32 [B,Nq,Hq,d], LSE fp32 [B,Hq,Nq])."""
+    import torch
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _check_tensor(t, n, torch.float8_e4m3fn, 4)
+    B, Nq, Hq, d = q8.shape
+    Bk, Nk, Hkv, dk = k8.shape
+    if tuple(v8.shape) != tuple(k8.shape) or Bk != B or dk != d:
+        raise ValueError(f"shape mismatch: q {tuple(q8.shape)} k {tuple(k8.shape)} v {tuple(v8.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Nq, Hq, d), dtype=torch.float32, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q8.device)
+    _check_tensor(o, "o", torch.float32, 4)
+    _check_tensor(lse, "lse", torch.float32, 3)
+    if tuple(o.shape) != (B, Nq, Hq, d) or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("o / lse have the wrong shape")
+    st = lib().fa_forward_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq,
+                              Nk, d, float(scale), 1 if causal else 0, float(q_descale),
+                              float(k_descale), float(v_descale), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward_fp8")
+    return o, lse
 
 
 def _check_token_rows(t, name):

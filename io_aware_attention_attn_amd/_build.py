@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.hip", "fa_prefill_bf16.hip", "fa_prefill_f32.hip", "fa_decode.hip",
-           "fa_backward.hip"]
+           "fa_backward.hip", "fa_prefill_fp8.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

@@ -111,6 +111,20 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, float* o, flo
   return fa::launch_prefill_bf16(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_forward_fp8(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   float q_descale, float k_descale, float v_descale, hipStream_t stream) {
+  const int st = check_prefill(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal);
+  if (st != FA_OK) return st;
+  // descales must be positive finite numbers (NaN fails every comparison)
+  if (!(q_descale > 0.f && q_descale < 3.0e38f) || !(k_descale > 0.f && k_descale < 3.0e38f) ||
+      !(v_descale > 0.f && v_descale < 3.0e38f))
+    return FA_ERR_SHAPE;
+  fa::Fp8Args a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal ? 1 : 0,
+                q_descale, k_descale, v_descale};
+  return fa::launch_prefill_fp8(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_backward_workspace_bytes(int B, int Hq, int Nq) {
   if (B <= 0 || Hq <= 0 || Nq <= 0) return 0;
   return 2 * fa::backward_vec_bytes(B, Hq, Nq);
@@ -204,7 +218,8 @@ const char* fa_status_str(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (non-positive, Hq % Hkv != 0, causal "
-                              "with Nq > Nk, a packed row stride too small, or too large for 32-bit indexing)";
+                              "with Nq > Nk, a packed row stride too small, a descale not positive, or too large "
+                              "for 32-bit indexing)";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128; decode chunk "
                                     "and page size must be positive multiples of 64";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a tensor pointer is not 16-byte aligned (or a "

@@ -71,7 +71,21 @@ inline size_t backward_vec_bytes(int B, int Hq, int Nq) {
   return (n + 255) & ~(size_t)255;
 }
 
+// FP8 forward: q [B,Nq,Hq,d], k, v [B,Nk,Hkv,d] as OCP E4M3 codes; value = code * descale.
+struct Fp8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  float q_descale, k_descale, v_descale;
+};
+
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+hipError_t launch_prefill_fp8(const Fp8Args& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t s);

@@ -35,7 +35,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert set(names) == {"fa_forward", "fa_forward_f32", "fa_forward_varlen",
+    assert set(names) == {"fa_forward", "fa_forward_f32", "fa_forward_fp8", "fa_forward_varlen",
                           "fa_backward_workspace_bytes", "fa_backward",
                           "fa_decode_splitkv_workspace_bytes",
                           "fa_decode_splitkv", "fa_decode_paged", "fa_status_str"}
@@ -79,6 +79,28 @@ def _fwd(L, entry, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64
 ])
 def test_forward_rejects(L, entry, kw, status):
     assert _fwd(L, entry, **kw) == status
+
+
+def _fp8(L, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, scale=0.125,
+         causal=0, qd=0.01, kd=0.02, vd=0.03):
+    return L.fa_forward_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, qd, kd, vd,
+                            None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(lse=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(Nq=9, causal=1), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(k=MIS), fa.FA_ERR_ALIGN),
+    (dict(qd=0.0), fa.FA_ERR_SHAPE),
+    (dict(kd=-1.0), fa.FA_ERR_SHAPE),
+    (dict(vd=float("nan")), fa.FA_ERR_SHAPE),
+    (dict(vd=float("inf")), fa.FA_ERR_SHAPE),
+])
+def test_fp8_rejects(L, kw, status):
+    assert _fp8(L, **kw) == status
 
 
 def _varlen(L, q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, B=2, Hq=4, Hkv=2, max_q=64, max_k=70,

@@ -159,6 +159,27 @@ def backward_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: i
     return tuple(t.to(torch.bfloat16) for t in (q, k, v, do))
 
 
+def fp8_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int = 0,
+               qk_gain: float = 1.0):
+    """FP8 (torch.float8_e4m3fn, OCP E4M3) Q, K, V with per-tensor descales, from the
+    same fp32 draws as ``prefill_inputs``: descale = max|x| / 448 (E4M3's largest
+    finite value), code = round-to-nearest-even(x / descale).  Returns
+    (q8, k8, v8, q_descale, k_descale, v_descale); the values are code * descale."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    xs = [torch.randn((B, Nq, Hq, d), generator=g, dtype=torch.float32),
+          torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32),
+          torch.randn((B, Nk, Hkv, d), generator=g, dtype=torch.float32)]
+    if qk_gain != 1.0:
+        xs[0].mul_(qk_gain)
+        xs[1].mul_(qk_gain)
+    codes, desc = [], []
+    for x in xs:
+        ds = float(x.abs().max()) / 448.0
+        codes.append((x / ds).to(torch.float8_e4m3fn))
+        desc.append(ds)
+    return (*codes, *desc)
+
+
 def prefill_inputs_for(cfg: PrefillConfig, seed: int = 0):
     return prefill_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.dtype, seed,
                           cfg.qk_gain)
