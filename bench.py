@@ -412,7 +412,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, causal>",
                      "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": (profiled_traffic("prefill_bf16_kernel<128, 4, true>")
+                     "traffic": (profiled_traffic("prefill_bf16_kernel<128, 4, true, false>")
                                  if pcfg.d == 128 and pcfg.causal else None),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "avg_launch_ms": round(avg_pre, 4),
@@ -435,7 +435,7 @@ def main():
                                      "LSE merge of the pieces",
                             "bytes_per_call": dbytes,
                             "sum_seqlens": int(dec["lengths"].sum().item()),
-                            "traffic_split": profiled_traffic("decode_split_kernel<128>"),
+                            "traffic_split": profiled_traffic("decode_split_kernel<128, false>"),
                             "traffic_merge": profiled_traffic("decode_merge_kernel<128>")}
     if dec and not args.no_paged:
         result["decode_paged"] = bench_paged(fa, W, dcfg, dec, dev, K)

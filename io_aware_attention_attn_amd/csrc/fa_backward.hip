@@ -272,33 +272,27 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const char* qt = reinterpret_cast<const char*>(qs(st));
     const char* ot = reinterpret_cast<const char*>(os(st));
 
-    // S = Q K^T and dP = dO V^T for both 32-row halves (4 independent accumulators)
+    // per 32-row half: S = Q K^T and dP = dO V^T, then the softmax gradient, then the
+    // dV / dK products; written so half 1's products overlap half 0's VALU work
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int rh = 0; rh < 2; ++rh) {
+    u32x4 pw[4], dw[4];
+    const int kmin = key - diag - m;  // causal: tile row r sees this key iff r >= kmin
+    auto sdp = [&](int rh) __attribute__((always_inline)) {
       s[rh] = f32x16{};
       dp[rh] = f32x16{};
-    }
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int rh = 0; rh < 2; ++rh) {
+      for (int kk = 0; kk < D / 16; ++kk) {
         const int row = 32 * rh + l32;
         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + row_chunk<D>(row, 2 * kk + hi));
         const bf16x8 ao = *reinterpret_cast<const bf16x8*>(ot + row_chunk<D>(row, 2 * kk + hi));
         s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], s[rh], 0, 0, 0);
         dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], dp[rh], 0, 0, 0);
       }
-
-    // P = exp2(S c - lse2_row) (0 where the key is not visible), dS = P (dP - D_row);
-    // both packed to bf16 as B operands (k = rows in the register order of D)
-    const int kmin = key - diag - m;  // causal: tile row r sees this key iff r >= kmin
-    u32x4 pw[4], dw[4];
-#pragma unroll
-    for (int rh = 0; rh < 2; ++rh) {
+    };
+    auto grad = [&](int rh) __attribute__((always_inline)) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int r0 = 32 * rh + 8 * q4 + 4 * hi;  // tile rows r0 .. r0+3 of registers 4q4..
+        const int r0 = 32 * rh + 8 * q4 + 4 * hi;
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(&ls[st][0][r0]);
         const f32x4 dd = *reinterpret_cast<const f32x4*>(&ls[st][1][r0]);
         float pv[4], dv4[4];
@@ -309,7 +303,6 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           pv[t4] = p;
           dv4[t4] = p * (dp[rh][4 * q4 + t4] - dd[t4]);
         }
-        // registers 4q4 .. 4q4+3 are words 2(q4&1), +1 of B operand u (16-row step)
         const int u = 2 * rh + (q4 >> 1);
         const int w = 2 * (q4 & 1);
         pw[u][w] = pack_bf16x2(pv[0], pv[1]);
@@ -317,24 +310,27 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         dw[u][w] = pack_bf16x2(dv4[0], dv4[1]);
         dw[u][w + 1] = pack_bf16x2(dv4[2], dv4[3]);
       }
-    }
-    bf16x8 pp[4], dsp[4];
+    };
+    auto accum = [&](int rh) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      pp[u] = __builtin_bit_cast(bf16x8, pw[u]);
-      dsp[u] = __builtin_bit_cast(bf16x8, dw[u]);
-    }
-
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 rows (4 steps of 16)
+      for (int u = 2 * rh; u < 2 * rh + 2; ++u) {
+        const bf16x8 pp = __builtin_bit_cast(bf16x8, pw[u]);
+        const bf16x8 dsp = __builtin_bit_cast(bf16x8, dw[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 ao = tr_operand<D>(os(st), toff, db, u);
-        const bf16x8 aq = tr_operand<D>(qs(st), toff, db, u);
-        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pp[u], dvt[db], 0, 0, 0);
-        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsp[u], dkt[db], 0, 0, 0);
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 ao = tr_operand<D>(os(st), toff, db, u);
+          const bf16x8 aq = tr_operand<D>(qs(st), toff, db, u);
+          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pp, dvt[db], 0, 0, 0);
+          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsp, dkt[db], 0, 0, 0);
+        }
       }
+    };
+    sdp(0);
+    sdp(1);
+    grad(0);
+    accum(0);
+    grad(1);
+    accum(1);
     (void)m;
   }
 
@@ -360,7 +356,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // dQ for 128 query rows (32 per wave) of one (batch, query head).
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(1, 1))) void
+                          amdgpu_waves_per_eu(2, 2))) void
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ Dws, const float* __restrict__ L2ws,
@@ -452,58 +448,60 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const char* kt = reinterpret_cast<const char*>(ks(st));
     const char* vt = reinterpret_cast<const char*>(vs(st));
 
-    // S^T = K Q^T and dP^T = V dO^T: keys 32kb + (register order), lane = query row
+    // per 32-key half: S^T = K Q^T and dP^T = V dO^T (lane = query row), then dS^T, then
+    // dQ^T += K^T dS^T; half 1's products overlap half 0's VALU work
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    bf16x8 dsp[4];
+    const int lim = CAUSAL ? min(qrow + diag, Nk - 1) - j * kTile - 4 * hi
+                           : Nk - 1 - j * kTile - 4 * hi;
+    auto sdp = [&](int kb) __attribute__((always_inline)) {
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
-    }
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kk = 0; kk < D / 16; ++kk) {
         const int row = 32 * kb + l32;
         const bf16x8 ak = *reinterpret_cast<const bf16x8*>(kt + row_chunk<D>(row, 2 * kk + hi));
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + row_chunk<D>(row, 2 * kk + hi));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], s[kb], 0, 0, 0);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], dp[kb], 0, 0, 0);
       }
-
-    // dS^T = P^T (dP^T - D) with P^T = exp2(S^T c - lse2); keys past the end or (causal)
-    // past this row's last visible key get P = 0
-    const int lim = CAUSAL ? min(qrow + diag, Nk - 1) - j * kTile - 4 * hi
-                           : Nk - 1 - j * kTile - 4 * hi;
-    bf16x8 dsp[4];
+    };
+    auto grad = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kb = u >> 1;
-      const int base = 8 * (u & 1);
-      u32x4 w;
+      for (int u = 2 * kb; u < 2 * kb + 2; ++u) {
+        const int base = 8 * (u & 1);
+        u32x4 w;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float v2[2];
+        for (int t = 0; t < 4; ++t) {
+          float v2[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = base + 2 * t + e;
-          const int kl = kb * 32 + 8 * (r >> 2) + (r & 3);
-          float p = fast_exp2(fmaf(s[kb][r], c, -l2));
-          p = (kl <= lim) ? p : 0.f;
-          v2[e] = p * (dp[kb][r] - dd);
+          for (int e = 0; e < 2; ++e) {
+            const int r = base + 2 * t + e;
+            const int kl = kb * 32 + 8 * (r >> 2) + (r & 3);
+            float p = fast_exp2(fmaf(s[kb][r], c, -l2));
+            p = (kl <= lim) ? p : 0.f;
+            v2[e] = p * (dp[kb][r] - dd);
+          }
+          w[t] = pack_bf16x2(v2[0], v2[1]);
         }
-        w[t] = pack_bf16x2(v2[0], v2[1]);
+        dsp[u] = __builtin_bit_cast(bf16x8, w);
       }
-      dsp[u] = __builtin_bit_cast(bf16x8, w);
-    }
-
-    // dQ^T += K^T dS^T, K^T through transposed reads of the K tile
+    };
+    auto accum = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 2 * kb; u < 2 * kb + 2; ++u)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 a = tr_operand<D>(ks(st), toff, db, u);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsp[u], acc[db], 0, 0, 0);
-      }
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 a = tr_operand<D>(ks(st), toff, db, u);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsp[u], acc[db], 0, 0, 0);
+        }
+    };
+    sdp(0);
+    sdp(1);
+    grad(0);
+    accum(0);
+    grad(1);
+    accum(1);
   }
 
   if (qrow < Nq) {
