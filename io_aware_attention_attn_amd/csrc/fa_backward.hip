@@ -280,13 +280,17 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     auto sdp = [&](int rh) __attribute__((always_inline)) {
       s[rh] = f32x16{};
       dp[rh] = f32x16{};
+      bf16x8 aq[D / 16], ao[D / 16];
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         const int row = 32 * rh + l32;
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + row_chunk<D>(row, 2 * kk + hi));
-        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(ot + row_chunk<D>(row, 2 * kk + hi));
-        s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], s[rh], 0, 0, 0);
-        dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], dp[rh], 0, 0, 0);
+        aq[kk] = *reinterpret_cast<const bf16x8*>(qt + row_chunk<D>(row, 2 * kk + hi));
+        ao[kk] = *reinterpret_cast<const bf16x8*>(ot + row_chunk<D>(row, 2 * kk + hi));
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], kf[kk], s[rh], 0, 0, 0);
+        dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[kk], vf[kk], dp[rh], 0, 0, 0);
       }
     };
     auto grad = [&](int rh) __attribute__((always_inline)) {
@@ -312,16 +316,23 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
     };
     auto accum = [&](int rh) __attribute__((always_inline)) {
+      bf16x8 ao[2][D / 32], aq[2][D / 32];
 #pragma unroll
-      for (int u = 2 * rh; u < 2 * rh + 2; ++u) {
+      for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          ao[uu][db] = tr_operand<D>(os(st), toff, db, 2 * rh + uu);
+          aq[uu][db] = tr_operand<D>(qs(st), toff, db, 2 * rh + uu);
+        }
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int u = 2 * rh + uu;
         const bf16x8 pp = __builtin_bit_cast(bf16x8, pw[u]);
         const bf16x8 dsp = __builtin_bit_cast(bf16x8, dw[u]);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 ao = tr_operand<D>(os(st), toff, db, u);
-          const bf16x8 aq = tr_operand<D>(qs(st), toff, db, u);
-          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pp, dvt[db], 0, 0, 0);
-          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsp, dkt[db], 0, 0, 0);
+          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[uu][db], pp, dvt[db], 0, 0, 0);
+          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[uu][db], dsp, dkt[db], 0, 0, 0);
         }
       }
     };
