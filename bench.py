@@ -129,6 +129,39 @@ def cpu_baseline_prefill(cfg, target_s):
                       f"attention"}
 
 
+def cpu_baseline_backward(cfg, target_s):
+    """The fp64 oracle backward on a bounded sample of the same shape: dQ of the last R
+    query rows of the query heads of K/V head 0, R doubled until the sample takes
+    ~target_s; FLOP counted as for the GPU backward (2.5x the forward's per pair)."""
+    import torch
+    import oracle
+    import workloads as W
+    q, k, v, do = W.backward_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, seed=0,
+                                    qk_gain=cfg.qk_gain)
+    N, d, G = cfg.Nq, cfg.d, cfg.Hq // cfg.Hkv
+    R = 16
+    while True:
+        r0 = N - R
+        t0 = time.perf_counter()
+        oracle.attention_backward(q, k, v, do, cfg.scale, cfg.causal, kv_heads=[0], rows=(r0, N),
+                                  keys=(0, 0), row_block=64)
+        dt = time.perf_counter() - t0
+        if dt * 2 > target_s or R >= N:
+            break
+        R = min(N, R * 2)
+    if cfg.causal:
+        keys = sum(min(cfg.Nk, i + (cfg.Nk - cfg.Nq) + 1) for i in range(r0, N))
+    else:
+        keys = R * cfg.Nk
+    keys *= G
+    flops = 2.5 * 4.0 * d * keys
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{cfg.name}: dQ of query rows {r0}..{N - 1} of the {G} query heads of K/V "
+                      f"head 0 ({keys} visible (row,key) pairs), fp64 torch CPU (P, dP, dS "
+                      f"materialised)"}
+
+
 def bench_paged(fa, W, dcfg, dec, dev, K, page_size=256):
     """The same decode step with the KV cache scattered over a permuted pool of
     `page_size`-key pages (paged KV cache), timed on its own after the step."""
@@ -453,6 +486,8 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_prefill(pcfg, args.cpu_seconds)
+        if "backward" in result:
+            result["backward"]["cpu_baseline"] = cpu_baseline_backward(pcfg, args.cpu_seconds / 3)
         if dec:
             result["decode"]["cpu_baseline"] = cpu_baseline_decode(
                 dcfg, dec["lengths"], dec["q"], dec["kc"], dec["vc"], args.cpu_seconds / 3)
