@@ -132,7 +132,8 @@ def cpu_baseline_prefill(cfg, target_s):
 def cpu_baseline_backward(cfg, target_s):
     """The fp64 oracle backward on a bounded sample of the same shape: dQ of the last R
     query rows of the query heads of K/V head 0, R doubled until the sample takes
-    ~target_s; FLOP counted as for the GPU backward (2.5x the forward's per pair)."""
+    ~target_s.  FLOP counted for what the sample computes: the S, dP and dQ products
+    (3 of the backward's 5), 6 d per visible (row, key) pair."""
     import torch
     import oracle
     import workloads as W
@@ -154,12 +155,12 @@ def cpu_baseline_backward(cfg, target_s):
     else:
         keys = R * cfg.Nk
     keys *= G
-    flops = 2.5 * 4.0 * d * keys
+    flops = 6.0 * d * keys
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"{cfg.name}: dQ of query rows {r0}..{N - 1} of the {G} query heads of K/V "
-                      f"head 0 ({keys} visible (row,key) pairs), fp64 torch CPU (P, dP, dS "
-                      f"materialised)"}
+                      f"head 0 ({keys} visible (row,key) pairs; S, dP, dQ products = 6 d FLOP "
+                      f"per pair), fp64 torch CPU (P, dP, dS materialised)"}
 
 
 def bench_paged(fa, W, dcfg, dec, dev, K, page_size=256):
