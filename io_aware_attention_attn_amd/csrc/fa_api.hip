@@ -46,9 +46,8 @@ int check_decode_sizes(int B, int Hq, int Hkv, int Nk_max, int d, int chunk) {
   if ((long long)B * Nk_max * Hkv > INT_MAX) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (chunk <= 0 || chunk % 64 != 0) return FA_ERR_UNSUPPORTED;
-  const long long G = Hq / Hkv;
   // the split kernel counts all 64-key steps of all (batch, K/V head, head group)
-  // segments in 32-bit integers; Hkv * ceil(G / 16) <= Hq bounds the segment count
+  // segments in 32-bit integers; Hkv * ceil((Hq / Hkv) / 16) <= Hq bounds the segment count
   const long long steps = (long long)B * Hq * ((Nk_max + 63) / 64);
   if (steps > 0x3fffffffLL || Hq > 65535 || B > 65535) return FA_ERR_SHAPE;
   return FA_OK;

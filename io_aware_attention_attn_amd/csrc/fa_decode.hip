@@ -107,7 +107,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int g = lane >> 4;
   const int G = Hq / Hkv;
   const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
-  const int per_batch_group = Hkv * QG;
 
   // ---- per-lane fixed offsets
   // K fragment (A of S^T): key 16*kb + l16 of the step, d = 32*st + 8*g.
