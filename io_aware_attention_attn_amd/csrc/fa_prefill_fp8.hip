@@ -58,8 +58,10 @@ __device__ __forceinline__ int a_row_key(int l32, int kb) {
 
 // XOR of the 16-byte chunk index within a tile row (rows of D bytes).
 // K rows are read 32 bytes per lane in the permuted order above: the 16 rows a 16-lane
-// group reads at one chunk land on distinct bank groups.  V rows are read transposed,
-// 8 consecutive rows x one chunk per group: those 8 rows land on distinct bank groups.
+// group reads at one chunk land on distinct bank groups.  V rows are read transposed:
+// the two 16-lane groups of a half-wave read the same 8 consecutive rows at the adjacent
+// chunks 2c and 2c + 1, and the swizzle (even values only) keeps all 16 (row, chunk)
+// pairs on distinct bank groups.
 template <int D>
 __device__ __forceinline__ int swz_k8(int row) {
   return D == 128 ? (((row >> 1) & 1) | (((row >> 3) & 1) << 1) | (((row >> 5) & 1) << 2))
@@ -67,7 +69,7 @@ __device__ __forceinline__ int swz_k8(int row) {
 }
 template <int D>
 __device__ __forceinline__ int swz_v8(int row) {
-  return D == 128 ? ((row >> 1) & 3) : ((row >> 2) & 1);
+  return D == 128 ? (((row >> 1) & 3) << 1) : (((row >> 2) & 1) << 1);
 }
 
 // LDS-DMA of one 64-row block (D bytes per row) in 16-byte pieces, swizzled.
