@@ -26,6 +26,8 @@
 // k = 8(l/32) .. +7; B is column l%32, the same k; D holds column l%32, rows
 // 8(r/4) + 4(l/32) + r%4 in register r.  Tiles in LDS are read both as rows (16-byte
 // reads) and transposed (ds_read_b64_tr_b16), so one XOR swizzle serves both.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -37,6 +39,7 @@ constexpr int kTile = 64;  // rows per LDS tile (keys for dQ, query rows for dK/
 
 typedef __attribute__((address_space(3))) void blds_void_t;
 typedef __bf16 bbf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) bbf16x4 blds_bf16x4_t;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, uint32_t bytes) {
@@ -209,7 +212,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
   const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
 
-  // K^T and V^T fragments of this lane's key (B operands; zeros past Nk)
+  // K^T and -V^T fragments of this lane's key (B operands; zeros past Nk).  V enters
+  // negated (exact in bf16) so that the dP product, started from D instead of 0, yields
+  // D - dP directly: the softmax gradient needs no subtraction, and dK comes out negated.
   bf16x8 kf[D / 16], vf[D / 16];
   {
     const __amdgpu_buffer_rsrc_t rk =
@@ -220,15 +225,18 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int st = 0; st < D / 16; ++st) {
       const uint32_t off = (uint32_t)key * kv_row_bytes + (uint32_t)(16 * st + 8 * hi) * 2;
       kf[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vf[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+      vf[st] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0) ^ 0x80008000u);
     }
   }
 
-  // query tiles that can see any of the 128 keys: rows >= n0 - diag under the causal mask
-  const int m_first = CAUSAL ? max(0, n0 - diag) / kTile : 0;
+  // query tiles that can see any of the 128 keys: rows >= n0 - diag under the causal
+  // mask; tiles from row n0 + 127 - diag on see all of them and need no mask
   const int n_mt = (Nq + kTile - 1) / kTile;
-  const int per_head = max(n_mt - m_first, 0);
-  const int n_it = per_head * G;
+  const int m_first = CAUSAL ? min(max(0, n0 - diag) / kTile, n_mt) : 0;
+  const int m_full = CAUSAL ? min((max(0, n0 + 127 - diag) + kTile - 1) / kTile, n_mt) : 0;
+  const int n_it = (n_mt - m_first) * G;
+  const int n_open = (n_mt - m_full) * G;  // the first n_open iterations are unmasked
 
   f32x16 dkt[D / 32], dvt[D / 32];
 #pragma unroll
@@ -242,10 +250,14 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   uint32_t tl[PW];
   tile_offsets<D>(tl, q_row_bytes, wave, lane);
 
-  // iteration t -> (query head, query tile); LDS-DMA of its Q, dO, lse2 and D rows
+  // iteration t -> query tile n_mt-1 - t/G, query head t%G of the group: the workgroups of
+  // one K/V head that run together all start at the last tile and step through the same
+  // Q and dO tiles in the same order, so each tile is fetched from HBM about once per
+  // XCD and then hit in its L2
+  auto tile_of = [&](int t) __attribute__((always_inline)) { return n_mt - 1 - t / G; };
   auto issue = [&](int t, int stage) __attribute__((always_inline)) {
-    const int hq = kvh * G + t / per_head;
-    const int m = (m_first + t % per_head) * kTile;
+    const int hq = kvh * G + t % G;
+    const int m = tile_of(t) * kTile;
     const __amdgpu_buffer_rsrc_t rq =
         brsrc(Q + ((size_t)b * Nq * Hq + hq) * D, (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
     const __amdgpu_buffer_rsrc_t ro =
@@ -262,24 +274,35 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  if (n_it > 0) issue(0, 0);
-  for (int t = 0; t < n_it; ++t) {
-    const int st = t & 1;
-    const int m = (m_first + t % per_head) * kTile;
+  // one iteration on LDS stage ST (a compile-time constant, so every LDS address is a
+  // loop-invariant register plus an immediate), with or without the causal mask
+  auto step = [&](auto ST, auto MASK, int t) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value;
+    constexpr bool masked = decltype(MASK)::value;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's part of tile t has landed
     __syncthreads();                      // ... everyone's; stage st^1 is free again
     if (t + 1 < n_it) issue(t + 1, st ^ 1);
     const char* qt = reinterpret_cast<const char*>(qs(st));
     const char* ot = reinterpret_cast<const char*>(os(st));
 
-    // per 32-row half: S = Q K^T and dP = dO V^T, then the softmax gradient, then the
-    // dV / dK products; written so half 1's products overlap half 0's VALU work
+    // per 32-row half: S = Q K^T and D - dP = D + dO (-V)^T, then the softmax gradient,
+    // then the dV / dK products; written so half 1's products overlap half 0's VALU work
     f32x16 s[2], dp[2];
     u32x4 pw[4], dw[4];
-    const int kmin = key - diag - m;  // causal: tile row r sees this key iff r >= kmin
+    const int kmin = key - diag - tile_of(t) * kTile;  // tile row r sees the key iff r >= kmin
     auto sdp = [&](int rh) __attribute__((always_inline)) {
       s[rh] = f32x16{};
-      dp[rh] = f32x16{};
+      {
+        // D of the rows this lane's accumulator registers hold: 8 q4 + 4 hi + 0..3
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&ls[st][1][32 * rh + 4 * hi]);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&ls[st][1][32 * rh + 8 + 4 * hi]);
+        const f32x4 d2 = *reinterpret_cast<const f32x4*>(&ls[st][1][32 * rh + 16 + 4 * hi]);
+        const f32x4 d3 = *reinterpret_cast<const f32x4*>(&ls[st][1][32 * rh + 24 + 4 * hi]);
+        const f32x8 d01 = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const f32x8 d23 = __builtin_shufflevector(d2, d3, 0, 1, 2, 3, 4, 5, 6, 7);
+        dp[rh] = __builtin_shufflevector(d01, d23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12,
+                                         13, 14, 15);
+      }
       bf16x8 aq[D / 16], ao[D / 16];
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
@@ -293,19 +316,19 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[kk], vf[kk], dp[rh], 0, 0, 0);
       }
     };
+    // P = 2^(S c - lse2) and -dS = P (D - dP), packed to bf16 as B operands
     auto grad = [&](int rh) __attribute__((always_inline)) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int r0 = 32 * rh + 8 * q4 + 4 * hi;
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(&ls[st][0][r0]);
-        const f32x4 dd = *reinterpret_cast<const f32x4*>(&ls[st][1][r0]);
         float pv[4], dv4[4];
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
           float p = fast_exp2(fmaf(s[rh][4 * q4 + t4], c, -l2[t4]));
-          if (CAUSAL) p = (r0 + t4 >= kmin) ? p : 0.f;
+          if (masked) p = (r0 + t4 >= kmin) ? p : 0.f;
           pv[t4] = p;
-          dv4[t4] = p * (dp[rh][4 * q4 + t4] - dd[t4]);
+          dv4[t4] = p * dp[rh][4 * q4 + t4];
         }
         const int u = 2 * rh + (q4 >> 1);
         const int w = 2 * (q4 & 1);
@@ -342,10 +365,28 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     accum(0);
     grad(1);
     accum(1);
-    (void)m;
-  }
+  };
 
-  // dK = scale * (Q^T dS)^T, dV = (dO^T P)^T; lane = key, registers hold 4 consecutive d
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Open = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, CAUSAL>;
+  // pairs of iterations, stage 0 then stage 1; the unmasked run is cut to an even length
+  // (a tile that needs no mask may still take the masked path)
+  if (n_it > 0) issue(0, 0);
+  int t = 0;
+  for (; t + 1 < (n_open & ~1); t += 2) {
+    step(S0{}, Open{}, t);
+    step(S1{}, Open{}, t + 1);
+  }
+  for (; t + 1 < n_it; t += 2) {
+    step(S0{}, Masked{}, t);
+    step(S1{}, Masked{}, t + 1);
+  }
+  if (t < n_it) step(S0{}, Masked{}, t);
+
+  // dK = scale * (Q^T dS)^T (the accumulator holds -Q^T dS), dV = (dO^T P)^T; lane = key,
+  // registers hold 4 consecutive d
   if (key < Nk) {
     float* krow = dK + (((size_t)b * Nk + key) * Hkv + kvh) * D;
     float* vrow = dV + (((size_t)b * Nk + key) * Hkv + kvh) * D;
@@ -355,8 +396,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * db + 8 * g + 4 * hi;
         *reinterpret_cast<f32x4*>(krow + col) =
-            f32x4{dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale,
-                  dkt[db][4 * g + 2] * scale, dkt[db][4 * g + 3] * scale};
+            f32x4{dkt[db][4 * g] * -scale, dkt[db][4 * g + 1] * -scale,
+                  dkt[db][4 * g + 2] * -scale, dkt[db][4 * g + 3] * -scale};
         *reinterpret_cast<f32x4*>(vrow + col) =
             f32x4{dvt[db][4 * g], dvt[db][4 * g + 1], dvt[db][4 * g + 2], dvt[db][4 * g + 3]};
       }
@@ -444,12 +485,19 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
 
+  // key tiles every row of the block sees in full (and that lie inside Nk) need no mask
+  const int n_open =
+      min(n, (CAUSAL ? min(m0 + diag, Nk - 1) + 1 : Nk) / kTile);
+
   if (n > 0) {
     tile_issue<D>(rk, tl, 0, ks(0), wave);
     tile_issue<D>(rv, tl, 0, vs(0), wave);
   }
-  for (int j = 0; j < n; ++j) {
-    const int st = j & 1;
+  // one key tile on LDS stage ST (compile-time, so LDS addresses fold into immediates),
+  // with or without the causal / key-range mask
+  auto step = [&](auto ST, auto MASK, int j) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value;
+    constexpr bool masked = decltype(MASK)::value;
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
     if (j + 1 < n) {
@@ -490,7 +538,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const int r = base + 2 * t + e;
             const int kl = kb * 32 + 8 * (r >> 2) + (r & 3);
             float p = fast_exp2(fmaf(s[kb][r], c, -l2));
-            p = (kl <= lim) ? p : 0.f;
+            if (masked) p = (kl <= lim) ? p : 0.f;
             v2[e] = p * (dp[kb][r] - dd);
           }
           w[t] = pack_bf16x2(v2[0], v2[1]);
@@ -513,7 +561,22 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     accum(0);
     grad(1);
     accum(1);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Open = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  int j = 0;
+  for (; j + 1 < (n_open & ~1); j += 2) {
+    step(S0{}, Open{}, j);
+    step(S1{}, Open{}, j + 1);
   }
+  for (; j + 1 < n; j += 2) {
+    step(S0{}, Masked{}, j);
+    step(S1{}, Masked{}, j + 1);
+  }
+  if (j < n) step(S0{}, Masked{}, j);
 
   if (qrow < Nq) {
     float* row = dQ + (((size_t)b * Nq + qrow) * Hq + hq) * D;
