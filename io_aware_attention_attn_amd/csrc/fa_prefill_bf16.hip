@@ -144,7 +144,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
                     int n_mblocks, Varlen vl) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int BM = 32 * WAVES;
-  constexpr int NT = WAVES * 64;
   // One array per stage: the compiler's wait insertion can then tell an LDS-DMA
   // write into one stage from reads of the other, and does not stall the reads of
   // the current block on the prefetch of the next one.
@@ -496,7 +495,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
       }
     if (hi == 0) LSE[lse0 + qrow] = (l_ex > 0.f) ? (m_ref + fast_log2(l_ex)) * kLn2 : kNegInf;
   }
-  (void)NT;
 }
 
 template <int D, int WAVES, bool CAUSAL, bool VARLEN>
