@@ -167,6 +167,30 @@ def test_backward_small(case):
             _check(f"dV b{b} kvh{kvh}", dv[b, :, kvh], rv[b, :, kvh], wv, qv, Nq * G)
 
 
+@pytest.mark.parametrize("case", [(1, 4, 2, 200, 200, 128, True, 4.0),
+                                  (1, 2, 1, 96, 300, 64, False, 6.0)],
+                         ids=["causal gain 4", "noncausal gain 6"])
+def test_backward_peaky(case):
+    """Q and K scaled up so that the scores are tens to hundreds apart: P is close to
+    one-hot, exp2(S c - lse2) would overflow without the LSE shift, and dS concentrates on
+    a few keys per row."""
+    B, Hq, Hkv, Nq, Nk, d, causal, gain = case
+    print(f"backward peaky case {case}", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = W.backward_inputs(B, Hq, Hkv, Nq, Nk, d, seed=12, qk_gain=gain)
+    o, lse = _oracle_fwd(q, k, v, scale, causal)
+    dq, dk, dv = _run_bwd(q, k, v, do, o, lse, scale, causal)
+    rq, rk, rv = oracle.attention_backward(q, k, v, do, scale, causal)
+    G = Hq // Hkv
+    for h in range(Hq):
+        w, quad = _bounds_dq(q, k, v, do, o, scale, causal, 0, h, 0, Nq)
+        _check(f"dQ h{h}", dq[0, :, h], rq[0, :, h], w, quad, Nk)
+    for kvh in range(Hkv):
+        (wk, qk), (wv, qv) = _bounds_dkdv(q, k, v, do, o, scale, causal, 0, kvh, 0, Nk)
+        _check(f"dK kvh{kvh}", dk[0, :, kvh], rk[0, :, kvh], wk, qk, Nq * G)
+        _check(f"dV kvh{kvh}", dv[0, :, kvh], rv[0, :, kvh], wv, qv, Nq * G)
+
+
 def test_backward_c2_full():
     """The causal MHA workload (B=2, H=12, N=2048, d=64) in full."""
     cfg = W.CONFIGS["c2"]

@@ -135,6 +135,10 @@ EDGE = [  # B, Nq, Nk, Hq, Hkv, d, causal, gain
     (1, 384, 384, 2, 2, 128, True, 3.0),   # very peaky scores: many max changes
     (3, 64, 64, 3, 3, 64, False, 2.0),
     (1, 1100, 1100, 2, 1, 128, True, 1.0),
+    # scores hundreds apart: exp would overflow without the reference shift, rows are
+    # close to one-hot, and nearly every block moves the reference
+    (1, 256, 256, 2, 1, 128, True, 10.0),
+    (2, 100, 500, 2, 2, 64, False, 10.0),
 ]
 
 
