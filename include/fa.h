@@ -239,6 +239,9 @@ size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int c
  *   workspace  device buffer of at least fa_decode_splitkv_workspace_bytes(...)
  *              bytes, 16-byte aligned, owned by the caller; its contents on entry
  *              do not matter and are overwritten.
+ * One sequence's K or V rows are addressed with 32-bit byte offsets:
+ * (Nk_max + 64) * Hkv * d * 2 must stay below 2^31 (FA_ERR_SHAPE otherwise; a larger
+ * cache goes through fa_decode_paged, which addresses page by page).
  * The two kernels run in order on `stream`; stream order is the only
  * synchronisation between them.  Returns FA_OK or a negative fa_status.
  */

@@ -162,6 +162,8 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   if (!q || !k_cache || !v_cache || !seqlens_k || !o || !lse) return FA_ERR_NULL;
   const int st = check_decode_sizes(B, Hq, Hkv, Nk_max, d, chunk);
   if (st != FA_OK) return st;
+  // one sequence's K or V rows are addressed with 32-bit byte offsets
+  if ((long long)(Nk_max + 64) * Hkv * d * 2 > INT_MAX) return FA_ERR_SHAPE;
   if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(o) ||
       (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return FA_ERR_ALIGN;

@@ -76,6 +76,8 @@ def _fwd(L, entry, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64
     (dict(v=MIS), fa.FA_ERR_ALIGN),
     (dict(o=MIS), fa.FA_ERR_ALIGN),
     (dict(B=1 << 20, Nq=1 << 12, Hq=1 << 10, Hkv=1 << 10, Nk=8), fa.FA_ERR_SHAPE),
+    # one batch slice of O at 2^31 bytes: (65280 + 256) x 64 heads x 128 x 4 B (65279 passes)
+    (dict(B=1, Hq=64, Hkv=8, Nq=65280, Nk=65280, d=128), fa.FA_ERR_SHAPE),
 ])
 def test_forward_rejects(L, entry, kw, status):
     assert _fwd(L, entry, **kw) == status
@@ -204,6 +206,9 @@ def _dec(L, q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nk_max=512, d=1
     (dict(B=0), fa.FA_ERR_SHAPE),
     (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
     (dict(Nk_max=0), fa.FA_ERR_SHAPE),
+    # one sequence's K rows past 2^31 bytes (32-bit offsets): (1048513 + 64) keys x 8 heads
+    # x 256 B
+    (dict(B=1, Hq=8, Hkv=8, Nk_max=1048513), fa.FA_ERR_SHAPE),
     (dict(d=100), fa.FA_ERR_UNSUPPORTED),
     (dict(chunk=100), fa.FA_ERR_UNSUPPORTED),
     (dict(chunk=0), fa.FA_ERR_UNSUPPORTED),

@@ -105,6 +105,55 @@ def test_c4_sampled():
              row_blocks=[(0, 256), (16320, 16450), (N - 256, N)])
 
 
+def test_prefill_max_offsets():
+    """The longest sequence the host accepts for Hq = 64, Hkv = 8, d = 128: one batch
+    slice of O just under 2^31 bytes (N = 65279, odd, so the last tile is ragged).  Rows at
+    both ends of the first and the last query head, causal, against the oracle on that
+    head's slice."""
+    B, Hq, Hkv, d = 1, 64, 8, 128
+    N = (2 ** 31 - 1) // (Hq * d * 4) - 256
+    assert N == 65279
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = W.prefill_inputs(B, Hq, Hkv, N, N, d, "bf16", seed=41)
+    o, lse = _run_forward(q, k, v, scale, True)
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    G = Hq // Hkv
+    for h in (0, Hq - 1):
+        qh, kh, vh = q[:, :, h:h + 1], k[:, :, h // G:h // G + 1], v[:, :, h // G:h // G + 1]
+        for (r0, r1) in ((0, 64), (N - 64, N)):
+            o_ref, lse_ref = oracle.attention(qh, kh, vh, scale, True, rows=(r0, r1),
+                                              row_block=64)
+            _cmp(o[:, r0:r1, h], lse[:, h, r0:r1], o_ref[:, r0:r1, 0], lse_ref[:, 0, r0:r1],
+                 TOL_BF16, f"N={N} head {h} rows {r0}:{r1}")
+
+
+def test_decode_max_offsets():
+    """One sequence filling the largest contiguous cache the host accepts for Hkv = 8,
+    d = 128: (Nk_max + 64) * Hkv * d * 2 just under 2^31 bytes, so the last K/V head's last
+    rows sit at byte offsets just below 2^31.  K/V heads 0 and 7 against the oracle on
+    their slices."""
+    B, Hq, Hkv, d = 1, 8, 8, 128
+    Nk_max = (2 ** 31 - 1) // (Hkv * d * 2) - 64
+    assert Nk_max == 1048511
+    scale = 1.0 / math.sqrt(d)
+    lengths, q, kc, vc = W.decode_inputs(B, Hq, Hkv, d, Nk_max, 0, 0, seed=42,
+                                         lengths=torch.tensor([Nk_max], dtype=torch.int32))
+    dev = _dev()
+    o = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev)
+    fa.fa_decode_splitkv(q.to(dev), kc.to(dev), vc.to(dev), lengths.to(dev), scale=scale,
+                         chunk=256, o=o, lse=lse)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    for h in (0, Hkv - 1):
+        o_ref, lse_ref = oracle.decode_attention(q[:, h:h + 1], kc[:, :, h:h + 1],
+                                                 vc[:, :, h:h + 1], lengths, scale)
+        _cmp(o[:, h:h + 1], lse[:, h:h + 1], o_ref, lse_ref, TOL_BF16,
+             f"decode Nk_max={Nk_max} K/V head {h}")
+
+
 def test_c5_decode_full():
     cfg = W.CONFIGS["c5"]
     lengths, q, kc, vc = W.decode_inputs_for(cfg)
