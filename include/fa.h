@@ -41,8 +41,10 @@
  *     Nq == Nk this is "token i sees tokens 0..i").  causal with Nq > Nk is
  *     rejected because some rows would see no key at all.
  *   - d (head dimension) must be 64 or 128.
- *   - Sizes: every (batch) slice of Q, K and V must stay below 2^31 bytes, and the
- *     grid is one-dimensional (FA_ERR_SHAPE otherwise).
+ *   - Sizes: one batch's rows are addressed with 32-bit byte offsets, sized for the
+ *     fp32 tensors of the same shape: (Nq + 256) * Hq * d * 4 and (Nk + 256) * Hkv * d * 4
+ *     must stay below 2^31 (FA_ERR_SHAPE otherwise; e.g. Nq <= 65279 at Hq = 64,
+ *     d = 128), and the grid is one-dimensional.
  *   - Thread safety: every function may be called concurrently from several
  *     host threads; calls on one stream execute in stream order.
  */
