@@ -6,7 +6,9 @@ One step = one pass of the whole hot path on resident synthetic inputs:
   * decode:  fa_decode_splitkv on the GQA decode workload (bf16, B=16, Hq=64,
     Hkv=8, d=128, per-sequence key counts ~U[4096, 32768], chunk=256: key work
     split over the waves in runs of at least 256 keys) — the split kernel and
-    the merge kernel.
+    the merge kernel.  The K and V caches come from the library's allocation helper
+    (kv_cache_empty: one buffer, V 256 bytes off K's 1 KiB congruence class); the same
+    decode on two separate allocations is timed as well and reported beside it.
 `value` is the prefill's algorithmic TFLOP/s (4*B*Hq*Nq*Nk*d / 2 for causal) over
 its measured kernel time; the decode's HBM GB/s (compulsory K/V/q/O/LSE bytes)
 is reported alongside, and so are the paged-KV decode, the packed variable-length
@@ -16,7 +18,7 @@ step.  Kernel times come from HIP events recorded on the
 stream the kernels are launched on (torch's current stream), around every
 launch of the timed region.
 
-Prints ONE JSON line.  `python bench.py --gpus N` with N > 1 exits: this build
+Prints ONE JSON line.  `python bench.py --gpus N` with N > 1 exits: the library
 runs on one GPU only.
 """
 from __future__ import annotations
@@ -168,9 +170,12 @@ def bench_paged(fa, W, dcfg, dec, dev, K, page_size=256):
     `page_size`-key pages (paged KV cache), timed on its own after the step."""
     import torch
     print("[bench] paged decode", file=sys.stderr, flush=True)
-    kp, vp, table = W.paged_from_contiguous(dec["kc"], dec["vc"], dec["lengths"], page_size,
-                                            seed=7, spare_pages=9)
-    kp, vp, table = kp.to(dev), vp.to(dev), table.to(dev)
+    kp_h, vp_h, table = W.paged_from_contiguous(dec["kc"], dec["vc"], dec["lengths"], page_size,
+                                                seed=7, spare_pages=9)
+    kp, vp = fa.kv_cache_empty(kp_h.shape, device=dev)  # page pools laid out as the caches
+    kp.copy_(kp_h.to(dev))
+    vp.copy_(vp_h.to(dev))
+    table = table.to(dev)
     o = torch.empty_like(dec["o"])
     lse = torch.empty_like(dec["lse"])
     nbytes = fa.fa_decode_splitkv_workspace_bytes(dcfg.B, dcfg.Hq, table.shape[1] * page_size,
@@ -199,6 +204,40 @@ def bench_paged(fa, W, dcfg, dec, dev, K, page_size=256):
             "median_call_ms": round(sorted(ms)[K // 2], 4), "page_size": page_size,
             "pool_pages": int(kp.shape[0]),
             "layout": "c5 keys in a seeded permutation of a page pool, block table per sequence"}
+
+
+def bench_decode_separate(fa, W, dcfg, dec, dev, K):
+    """The decode step with the K and V caches as two separate allocations (each 2 MiB
+    aligned, so their starts are congruent modulo 1 KiB), timed on its own: the layout
+    kv_cache_empty avoids, reported for comparison."""
+    import torch
+    print("[bench] decode, separate K/V allocations", file=sys.stderr, flush=True)
+    kc2, vc2 = dec["kc"].to(dev), dec["vc"].to(dev)
+    o = torch.empty_like(dec["o"])
+    lse = torch.empty_like(dec["lse"])
+
+    def call():
+        fa.fa_decode_splitkv(dec["dq"], kc2, vc2, dec["dl"], scale=dcfg.scale,
+                             chunk=dcfg.chunk, o=o, lse=lse, workspace=dec["ws"])
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / K
+    dbytes = W.decode_bytes(dec["lengths"].tolist(), dcfg.Hq, dcfg.Hkv, dcfg.d)
+    gbs = dbytes / (avg * 1e-3) / 1e9
+    rel = (vc2.data_ptr() - kc2.data_ptr()) % 1024
+    del kc2, vc2
+    torch.cuda.empty_cache()
+    return {"value": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "avg_call_ms": round(avg, 4), "v_minus_k_mod_1KiB": int(rel)}
 
 
 def bench_varlen(fa, W, dev, K):
@@ -346,7 +385,7 @@ def cpu_baseline_decode(cfg, lengths, q, kc, vc, target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on exactly one GPU; --gpus {args.gpus} is not supported "
               f"(no collectives or sharding are implemented).", file=sys.stderr)
         sys.exit(2)
     import torch
@@ -370,8 +409,13 @@ def main():
     if not args.no_decode:
         print(f"[bench] generating {dcfg.name} inputs", file=sys.stderr, flush=True)
         lengths, dq, kc, vc = W.decode_inputs_for(dcfg)
+        # K and V caches from the library's allocation helper (one buffer, V 256 bytes off
+        # the K cache's 1 KiB congruence class); the two-allocation layout is timed too
+        dkc, dvc = fa.kv_cache_empty(kc.shape, device=dev)
+        dkc.copy_(kc.to(dev))
+        dvc.copy_(vc.to(dev))
         dec = dict(lengths=lengths, q=dq, kc=kc, vc=vc,
-                   dq=dq.to(dev), dkc=kc.to(dev), dvc=vc.to(dev), dl=lengths.to(dev))
+                   dq=dq.to(dev), dkc=dkc, dvc=dvc, dl=lengths.to(dev))
         dec["o"] = torch.empty((dcfg.B, dcfg.Hq, dcfg.d), dtype=torch.float32, device=dev)
         dec["lse"] = torch.empty((dcfg.B, dcfg.Hq), dtype=torch.float32, device=dev)
         nbytes = fa.fa_decode_splitkv_workspace_bytes(dcfg.B, dcfg.Hq, dcfg.Nk_max, dcfg.d,
@@ -470,7 +514,11 @@ def main():
                             "bytes_per_call": dbytes,
                             "sum_seqlens": int(dec["lengths"].sum().item()),
                             "traffic_split": profiled_traffic("decode_split_kernel<128, false>"),
-                            "traffic_merge": profiled_traffic("decode_merge_kernel<128>")}
+                            "traffic_merge": profiled_traffic("decode_merge_kernel<128>"),
+                            "cache_layout": "K and V caches in one allocation with V starting "
+                                            "256 B past K's 1 KiB congruence class "
+                                            "(kv_cache_empty)"}
+        result["decode"]["separate_allocations"] = bench_decode_separate(fa, W, dcfg, dec, dev, K)
     if dec and not args.no_paged:
         result["decode_paged"] = bench_paged(fa, W, dcfg, dec, dev, K)
     if not args.no_varlen or not args.no_backward or not args.no_fp8:

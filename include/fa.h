@@ -244,6 +244,13 @@ size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int c
  * One sequence's K or V rows are addressed with 32-bit byte offsets:
  * (Nk_max + 64) * Hkv * d * 2 must stay below 2^31 (FA_ERR_SHAPE otherwise; a larger
  * cache goes through fa_decode_paged, which addresses page by page).
+ * Placement (performance only): the split kernel reads the K row and the V row of one
+ * token and head at the same time, and they are v_cache - k_cache bytes apart.  When
+ * that distance is a multiple of 1 KiB (two separately allocated, 2 MiB-aligned caches)
+ * those reads fall in the same 256-byte address class and the kernel streams about 5%
+ * slower on MI355X; any other distance modulo 1 KiB avoids it (the Python helper
+ * kv_cache_empty puts V 256 bytes past that class).  The same holds for the page pools
+ * of fa_decode_paged.
  * The two kernels run in order on `stream`; stream order is the only
  * synchronisation between them.  Returns FA_OK or a negative fa_status.
  */

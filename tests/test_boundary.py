@@ -274,3 +274,23 @@ def test_product_does_not_import_oracle():
         if f.endswith(".py"):
             src = open(os.path.join(ROOT, "oracle", f)).read()
             assert not imp_pkg.search(src), f
+
+
+@pytest.mark.parametrize("shape", [(16, 32768, 8, 128), (2, 700, 2, 64), (3, 100, 1, 64),
+                                   (1311, 256, 8, 128)])
+def test_kv_cache_empty_layout(shape):
+    """The allocation helper: two contiguous caches of the requested shape in one buffer,
+    not overlapping, both 16-byte aligned relative to the buffer, and the V cache 256 bytes
+    past the K cache's 1 KiB congruence class (on the CPU here; the device only changes
+    where the buffer lives)."""
+    torch = pytest.importorskip("torch")
+    k, v = fa.kv_cache_empty(shape, device="cpu")
+    assert tuple(k.shape) == shape and tuple(v.shape) == shape
+    assert k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16
+    assert k.is_contiguous() and v.is_contiguous()
+    nbytes = k.numel() * 2
+    delta = v.data_ptr() - k.data_ptr()
+    assert delta >= nbytes                      # no overlap
+    assert delta % 16 == 0                      # V keeps K's 16-byte alignment
+    assert delta % 1024 == fa.KV_V_OFFSET_MOD_1K == 256
+    assert delta - nbytes < 1024                # at most one KiB of padding

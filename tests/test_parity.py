@@ -312,6 +312,37 @@ def test_c5_decode_paged_full():
     _cmp(o, lse, o_ref, lse_ref, TOL_BF16, "c5 paged")
 
 
+def test_c5_decode_kv_cache_empty():
+    """The c5 decode on caches (contiguous, then a page pool) laid out by the library's
+    allocation helper, one buffer with V 256 bytes past K's 1 KiB congruence class: the
+    same results as the oracle (and bitwise the same as on separate allocations)."""
+    cfg = W.CONFIGS["c5"]
+    lengths, q, kc, vc = W.decode_inputs_for(cfg)
+    dev = _dev()
+    k2, v2 = fa.kv_cache_empty(kc.shape, device=dev)
+    k2.copy_(kc.to(dev))
+    v2.copy_(vc.to(dev))
+    assert (v2.data_ptr() - k2.data_ptr()) % 1024 == 256
+    qd, ld = q.to(dev), lengths.to(dev)
+    o, lse = fa.fa_decode_splitkv(qd, k2, v2, ld, scale=cfg.scale, chunk=cfg.chunk)
+    o_sep, lse_sep = fa.fa_decode_splitkv(qd, kc.to(dev), vc.to(dev), ld, scale=cfg.scale,
+                                          chunk=cfg.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_sep) and torch.equal(lse, lse_sep)
+    o_ref, lse_ref = oracle.decode_attention(q, kc, vc, lengths, cfg.scale)
+    _cmp(o.cpu(), lse.cpu(), o_ref, lse_ref, TOL_BF16, "c5 kv_cache_empty")
+    del k2, v2
+    kp, vp, table = W.paged_from_contiguous(kc, vc, lengths, 256, seed=7, spare_pages=9)
+    kp2, vp2 = fa.kv_cache_empty(kp.shape, device=dev)
+    kp2.copy_(kp.to(dev))
+    vp2.copy_(vp.to(dev))
+    o, lse = fa.fa_decode_paged(qd, kp2, vp2, table.to(dev), ld, scale=cfg.scale,
+                                chunk=cfg.chunk)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_attention_paged(q, kp, vp, table, lengths, 256, cfg.scale)
+    _cmp(o.cpu(), lse.cpu(), o_ref, lse_ref, TOL_BF16, "c5 paged kv_cache_empty")
+
+
 PAGED = [  # B, Hq, Hkv, d, page_size, lengths, chunk
     (3, 8, 2, 128, 64, [1, 64, 130], 64),
     (4, 16, 2, 64, 128, [127, 128, 129, 600], 256),
