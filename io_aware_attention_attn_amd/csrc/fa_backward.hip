@@ -310,6 +310,10 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         aq[kk] = *reinterpret_cast<const bf16x8*>(qt + row_chunk<D>(row, 2 * kk + hi));
         ao[kk] = *reinterpret_cast<const bf16x8*>(ot + row_chunk<D>(row, 2 * kk + hi));
       }
+      // all 16 operand reads go out before the first product: left to itself the compiler
+      // issues each read just ahead of its MFMA and the one wave per SIMD then waits out
+      // the LDS latency before every product
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], kf[kk], s[rh], 0, 0, 0);
@@ -347,6 +351,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           ao[uu][db] = tr_operand<D>(os(st), toff, db, 2 * rh + uu);
           aq[uu][db] = tr_operand<D>(qs(st), toff, db, 2 * rh + uu);
         }
+      __builtin_amdgcn_sched_barrier(0);  // likewise: the 32 transposed reads first
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
         const int u = 2 * rh + uu;
