@@ -165,12 +165,30 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   const int T = n_mblocks * B * Hq;
   const int lam = xcd_remap((int)blockIdx.x, T);
   int hg, mb, kvh, b;
-  if (!VARLEN) {
-    // equal sequences: (batch, K/V head) major, the group's heads adjacent per query block
+  const int NBK = B * Hkv;          // (batch, K/V head) groups
+  const int NB = n_mblocks * NBK;   // bundles: one query block of the G heads of one group
+  if (!VARLEN && (NBK % kNumXcd == 0 || NB % kNumXcd != 0)) {
+    // equal sequences, whole groups per XCD: (batch, K/V head) major, the group's heads
+    // adjacent per query block
     hg = lam % G;
     const int rest = lam / G;
     mb = n_mblocks - 1 - rest % n_mblocks;
     const int bk = rest / n_mblocks;
+    kvh = bk % Hkv;
+    b = bk / Hkv;
+  } else if (!VARLEN) {
+    // equal sequences, groups not a multiple of the XCD count: a group's query blocks would
+    // split unevenly (one XCD the heavy causal blocks, the next the light ones), so the
+    // bundles, heaviest first, are dealt to the XCDs in a snake (0..7, 7..0, ...): every XCD
+    // gets the same work to within one bundle and still runs its share heaviest first.
+    // Workgroup i of XCD x (blockIdx = 8 i + x) takes head hg = i % G of its bundle i / G.
+    const int x = (int)blockIdx.x % kNumXcd;
+    const int i = (int)blockIdx.x / kNumXcd;
+    const int j = i / G;
+    hg = i % G;
+    const int gb = j * kNumXcd + ((j & 1) ? kNumXcd - 1 - x : x);
+    mb = n_mblocks - 1 - gb / NBK;
+    const int bk = gb % NBK;
     kvh = bk % Hkv;
     b = bk / Hkv;
   } else if (Hkv % kNumXcd == 0) {

@@ -136,14 +136,30 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
   const int hi = lane >> 5;
 
   // work order as the bf16 prefill: (batch, K/V head) major, heaviest query block first,
-  // the GQA group's query heads adjacent; each XCD gets a contiguous slice
+  // the GQA group's query heads adjacent; each XCD gets a contiguous slice.  When the
+  // groups do not divide over the XCDs, the bundles (one query block of one group's G
+  // heads), heaviest first, are dealt to the XCDs in a snake (0..7, 7..0, ...) instead, so
+  // that no XCD gets only the heavy causal blocks of a group.
   const int G = Hq / Hkv;
   const int T = n_mblocks * B * Hq;
-  const int lam = xcd_remap8((int)blockIdx.x, T);
-  const int hg = lam % G;
-  const int rest = lam / G;
-  const int mb = n_mblocks - 1 - rest % n_mblocks;
-  const int bk = rest / n_mblocks;
+  const int NBK = B * Hkv;
+  const int NB = n_mblocks * NBK;
+  int hg, mb, bk;
+  if (NBK % kXcd8 == 0 || NB % kXcd8 != 0) {
+    const int lam = xcd_remap8((int)blockIdx.x, T);
+    hg = lam % G;
+    const int rest = lam / G;
+    mb = n_mblocks - 1 - rest % n_mblocks;
+    bk = rest / n_mblocks;
+  } else {
+    const int x = (int)blockIdx.x % kXcd8;
+    const int i = (int)blockIdx.x / kXcd8;  // workgroup i of XCD x
+    const int j = i / G;
+    hg = i % G;
+    const int gb = j * kXcd8 + ((j & 1) ? kXcd8 - 1 - x : x);
+    mb = n_mblocks - 1 - gb / NBK;
+    bk = gb % NBK;
+  }
   const int kvh = bk % Hkv;
   const int b = bk / Hkv;
   const int hq = kvh * G + hg;

@@ -144,6 +144,10 @@ SMALL = [
     (1, 2, 2, 1, 65, 64, True),
     (1, 16, 1, 130, 130, 64, True),
     (2, 2, 1, 257, 190, 128, False),
+    # groups that do not divide over the 8 XCDs while the key / query blocks do (snake
+    # assignment of work to XCDs in both gradient kernels)
+    (1, 8, 2, 1024, 1024, 128, True),
+    (1, 3, 1, 1000, 1000, 64, True),
 ]
 
 

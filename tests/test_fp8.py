@@ -94,6 +94,7 @@ SMALL = [
     (1, 8, 2, 77, 333, 128, True),
     (1, 2, 2, 1, 65, 64, True),
     (2, 2, 1, 257, 190, 128, False),
+    (1, 8, 2, 1024, 1024, 128, True),  # snake assignment of work to XCDs
 ]
 
 

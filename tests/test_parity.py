@@ -188,6 +188,11 @@ EDGE = [  # B, Nq, Nk, Hq, Hkv, d, causal, gain
     # close to one-hot, and nearly every block moves the reference
     (1, 256, 256, 2, 1, 128, True, 10.0),
     (2, 100, 500, 2, 2, 64, False, 10.0),
+    # (batch, K/V head) groups that do not divide over the 8 XCDs while their query blocks
+    # do: the workgroups take the snake assignment of bundles to XCDs
+    (1, 1024, 1024, 8, 2, 128, True, 1.0),
+    (2, 512, 700, 6, 3, 64, True, 1.0),
+    (1, 1000, 1000, 4, 1, 128, True, 1.0),
 ]
 
 
