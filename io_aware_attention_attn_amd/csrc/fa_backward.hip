@@ -34,7 +34,6 @@
 namespace fa {
 namespace {
 
-constexpr int kXcd = 8;   // workgroups dispatched round-robin over 8 XCDs
 constexpr int kTile = 64;  // rows per LDS tile (keys for dQ, query rows for dK/dV)
 
 typedef __attribute__((address_space(3))) void blds_void_t;
@@ -45,34 +44,6 @@ typedef __attribute__((address_space(3))) bbf16x4 blds_bf16x4_t;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
-}
-
-// Work item i of T, renumbered so each XCD receives a contiguous range of items.
-__device__ __forceinline__ int bxcd_remap(int g, int T) {
-  const int q = T / kXcd, r = T % kXcd;
-  const int x = g % kXcd, i = g / kXcd;
-  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-}
-
-// When the NBK = B * Hkv (batch, K/V head) groups do not divide over the XCDs (but their
-// n_blk * NBK bundles do), contiguous slices would hand one XCD the heavy causal blocks of
-// a group and the next the light ones.  Then the bundles, heaviest first (bundle gb: block
-// level gb / NBK counted from the heaviest, group gb % NBK), are dealt to the XCDs in a
-// snake (0..7, 7..0, ...) and each bundle is `per` consecutive workgroups of one XCD.
-// Sets blk = n_blk - 1 - (the bundle's level), i.e. the block in the forward's numbering
-// where block n_blk - 1 is the heaviest.  Returns false (and sets nothing) when the
-// contiguous slices are balanced already.
-__device__ __forceinline__ bool bxcd_snake(int g, int per, int NBK, int n_blk, int& sub,
-                                           int& blk, int& bk) {
-  const int NB = n_blk * NBK;
-  if (NBK % kXcd == 0 || NB % kXcd != 0) return false;
-  const int x = g % kXcd, i = g / kXcd;  // workgroup i of XCD x
-  const int j = i / per;
-  sub = i % per;
-  const int gb = j * kXcd + ((j & 1) ? kXcd - 1 - x : x);
-  blk = n_blk - 1 - gb / NBK;
-  bk = gb % NBK;
-  return true;
 }
 
 // XOR applied to the 16-byte chunk index of a tile row.  Row reads: 16 consecutive rows
@@ -220,16 +191,10 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int hi = lane >> 5;
 
   const int G = Hq / Hkv;
-  const int T = n_kblocks * B * Hkv;
-  // key blocks heaviest (seen by the most query rows) first
-  int kblk, bk, unused;
-  if (bxcd_snake((int)blockIdx.x, 1, B * Hkv, n_kblocks, unused, kblk, bk)) {
-    kblk = n_kblocks - 1 - kblk;  // here key block 0 is the heaviest
-  } else {
-    const int lam = bxcd_remap((int)blockIdx.x, T);
-    kblk = lam % n_kblocks;
-    bk = lam / n_kblocks;
-  }
+  // one workgroup per bundle; key block 0 (seen by the most query rows) is the heaviest
+  const XcdWork w = xcd_work((int)blockIdx.x, 1, B * Hkv, n_kblocks);
+  const int kblk = w.level;
+  const int bk = w.group;
   const int kvh = bk % Hkv;
   const int b = bk / Hkv;
   const int n0 = kblk * 128;
@@ -460,19 +425,13 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // work order as in the forward: (batch, K/V head) major, heaviest query block first,
-  // the group's query heads adjacent; bundles dealt to the XCDs in a snake when the groups
-  // do not divide over them
+  // work order as in the forward: bundles of one query block of one (batch, K/V head)
+  // group's G query heads, heaviest (last) query block first
   const int G = Hq / Hkv;
-  const int T = n_mblocks * B * Hq;
-  int hg, mb, bk;
-  if (!bxcd_snake((int)blockIdx.x, G, B * Hkv, n_mblocks, hg, mb, bk)) {
-    const int lam = bxcd_remap((int)blockIdx.x, T);
-    hg = lam % G;
-    const int rest = lam / G;
-    mb = n_mblocks - 1 - rest % n_mblocks;
-    bk = rest / n_mblocks;
-  }
+  const XcdWork w = xcd_work((int)blockIdx.x, G, B * Hkv, n_mblocks);
+  const int hg = w.sub;
+  const int mb = n_mblocks - 1 - w.level;
+  const int bk = w.group;
   const int kvh = bk % Hkv;
   const int b = bk / Hkv;
   const int hq = kvh * G + hg;

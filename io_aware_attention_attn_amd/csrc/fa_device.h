@@ -47,4 +47,49 @@ __device__ __forceinline__ u32x4 ldg128(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Work order over the XCDs.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup g runs on XCD g % 8 as that XCD's (g / 8)-th), and each XCD has its own L2.
+// The grid is NBK groups (a (batch, K/V head) pair: workgroups that stream the same K/V)
+// x n_blk block levels (level 0 the heaviest under the causal mask) x `per` workgroups per
+// bundle (one level of one group).  Where the groups divide over the XCDs, each XCD owns
+// whole groups and runs its share level by level, heaviest first; where they do not but
+// the bundles do, the bundles, heaviest first, are dealt to the XCDs in a snake (0..7,
+// 7..0, ...), so no XCD gets only the heavy blocks of a group; otherwise each XCD takes a
+// contiguous slice of the group-major list.
+constexpr int kXcds = 8;
+
+struct XcdWork {
+  int level;  // 0 = heaviest block
+  int group;  // (batch, K/V head) index
+  int sub;    // workgroup within the bundle
+};
+
+__device__ __forceinline__ XcdWork xcd_work(int g, int per, int NBK, int n_blk) {
+  const int x = g % kXcds, i = g / kXcds;  // workgroup i of XCD x
+  const int NB = n_blk * NBK;
+  XcdWork w;
+  if (NBK % kXcds == 0) {
+    const int gpx = NBK / kXcds;  // groups per XCD
+    const int r = i / per;
+    w.sub = i % per;
+    w.level = r / gpx;
+    w.group = x * gpx + r % gpx;
+  } else if (NB % kXcds == 0) {
+    const int j = i / per;
+    w.sub = i % per;
+    const int gb = j * kXcds + ((j & 1) ? kXcds - 1 - x : x);
+    w.level = gb / NBK;
+    w.group = gb % NBK;
+  } else {
+    const int T = NB * per;
+    const int q = T / kXcds, rm = T % kXcds;
+    const int lam = (x < rm) ? x * (q + 1) + i : rm * (q + 1) + (x - rm) * q + i;
+    w.sub = lam % per;
+    const int rest = lam / per;
+    w.level = rest % n_blk;
+    w.group = rest / n_blk;
+  }
+  return w;
+}
+
 }  // namespace fa

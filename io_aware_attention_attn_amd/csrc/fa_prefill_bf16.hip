@@ -57,7 +57,6 @@ namespace {
 
 constexpr int kBN = 64;        // keys per K/V block
 constexpr float kSumCap = 256.f;  // largest per-lane half-block sum of exp2(S*c - m_ref)
-constexpr int kNumXcd = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -118,8 +117,8 @@ __device__ __forceinline__ void issue_block(__amdgpu_buffer_rsrc_t rs, const uin
 }
 
 __device__ __forceinline__ int xcd_remap(int g, int T) {
-  const int q = T / kNumXcd, r = T % kNumXcd;
-  const int x = g % kNumXcd, i = g / kNumXcd;
+  const int q = T / kXcds, r = T % kXcds;
+  const int x = g % kXcds, i = g / kXcds;
   return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
@@ -160,40 +159,22 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- which work item: XCD slice, (batch, K/V head) major, heavy query blocks first
+  // ---- which work item: XCD-aware order, heavy query blocks first
   const int G = Hq / Hkv;
   const int T = n_mblocks * B * Hq;
-  const int lam = xcd_remap((int)blockIdx.x, T);
   int hg, mb, kvh, b;
-  const int NBK = B * Hkv;          // (batch, K/V head) groups
-  const int NB = n_mblocks * NBK;   // bundles: one query block of the G heads of one group
-  if (!VARLEN && (NBK % kNumXcd == 0 || NB % kNumXcd != 0)) {
-    // equal sequences, whole groups per XCD: (batch, K/V head) major, the group's heads
-    // adjacent per query block
-    hg = lam % G;
-    const int rest = lam / G;
-    mb = n_mblocks - 1 - rest % n_mblocks;
-    const int bk = rest / n_mblocks;
-    kvh = bk % Hkv;
-    b = bk / Hkv;
-  } else if (!VARLEN) {
-    // equal sequences, groups not a multiple of the XCD count: a group's query blocks would
-    // split unevenly (one XCD the heavy causal blocks, the next the light ones), so the
-    // bundles, heaviest first, are dealt to the XCDs in a snake (0..7, 7..0, ...): every XCD
-    // gets the same work to within one bundle and still runs its share heaviest first.
-    // Workgroup i of XCD x (blockIdx = 8 i + x) takes head hg = i % G of its bundle i / G.
-    const int x = (int)blockIdx.x % kNumXcd;
-    const int i = (int)blockIdx.x / kNumXcd;
-    const int j = i / G;
-    hg = i % G;
-    const int gb = j * kNumXcd + ((j & 1) ? kNumXcd - 1 - x : x);
-    mb = n_mblocks - 1 - gb / NBK;
-    const int bk = gb % NBK;
-    kvh = bk % Hkv;
-    b = bk / Hkv;
-  } else if (Hkv % kNumXcd == 0) {
+  if (!VARLEN) {
+    // equal sequences: bundles are one query block of one (batch, K/V head) group's G
+    // query heads, heaviest (last) query block first
+    const XcdWork w = xcd_work((int)blockIdx.x, G, B * Hkv, n_mblocks);
+    hg = w.sub;
+    mb = n_mblocks - 1 - w.level;
+    kvh = w.group % Hkv;
+    b = w.group / Hkv;
+  } else if (Hkv % kXcds == 0) {
     // unequal sequences: K/V head major, so each XCD's contiguous slice holds whole K/V
     // heads of every sequence (equal work per XCD), the group's heads adjacent
+    const int lam = xcd_remap((int)blockIdx.x, T);
     hg = lam % G;
     const int rest = lam / G;
     mb = n_mblocks - 1 - rest % n_mblocks;
@@ -202,6 +183,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     kvh = bk / B;
   } else {
     // fewer K/V heads than XCDs: query head major (balanced when Hq is a multiple of 8)
+    const int lam = xcd_remap((int)blockIdx.x, T);
     mb = n_mblocks - 1 - lam % n_mblocks;
     const int rest = lam / n_mblocks;
     b = rest % B;

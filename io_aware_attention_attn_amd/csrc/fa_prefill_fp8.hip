@@ -30,7 +30,6 @@ namespace {
 
 constexpr int kBN8 = 64;            // keys per K/V block
 constexpr float kSumCap8 = 256.f;   // largest per-lane block sum of exp2(S*c - m_ref)
-constexpr int kXcd8 = 8;
 constexpr int kOnesE4M3 = 0x38383838;  // four E4M3 1.0 codes
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -41,12 +40,6 @@ typedef __attribute__((address_space(3))) void lds8_void_t;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc8(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
-}
-
-__device__ __forceinline__ int xcd_remap8(int g, int T) {
-  const int q = T / kXcd8, r = T % kXcd8;
-  const int x = g % kXcd8, i = g / kXcd8;
-  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
 // Key row (within the 64-key block) that lane l32 feeds as A row of the S^T product for
@@ -135,31 +128,14 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // work order as the bf16 prefill: (batch, K/V head) major, heaviest query block first,
-  // the GQA group's query heads adjacent; each XCD gets a contiguous slice.  When the
-  // groups do not divide over the XCDs, the bundles (one query block of one group's G
-  // heads), heaviest first, are dealt to the XCDs in a snake (0..7, 7..0, ...) instead, so
-  // that no XCD gets only the heavy causal blocks of a group.
+  // work order as the bf16 prefill: bundles of one query block of one (batch, K/V head)
+  // group's G query heads, heaviest (last) query block first, spread over the XCDs by
+  // xcd_work
   const int G = Hq / Hkv;
-  const int T = n_mblocks * B * Hq;
-  const int NBK = B * Hkv;
-  const int NB = n_mblocks * NBK;
-  int hg, mb, bk;
-  if (NBK % kXcd8 == 0 || NB % kXcd8 != 0) {
-    const int lam = xcd_remap8((int)blockIdx.x, T);
-    hg = lam % G;
-    const int rest = lam / G;
-    mb = n_mblocks - 1 - rest % n_mblocks;
-    bk = rest / n_mblocks;
-  } else {
-    const int x = (int)blockIdx.x % kXcd8;
-    const int i = (int)blockIdx.x / kXcd8;  // workgroup i of XCD x
-    const int j = i / G;
-    hg = i % G;
-    const int gb = j * kXcd8 + ((j & 1) ? kXcd8 - 1 - x : x);
-    mb = n_mblocks - 1 - gb / NBK;
-    bk = gb % NBK;
-  }
+  const XcdWork w = xcd_work((int)blockIdx.x, G, B * Hkv, n_mblocks);
+  const int hg = w.sub;
+  const int mb = n_mblocks - 1 - w.level;
+  const int bk = w.group;
   const int kvh = bk % Hkv;
   const int b = bk / Hkv;
   const int hq = kvh * G + hg;
