@@ -41,10 +41,12 @@
 //     the next block's score MFMAs, the second the first half's P.V MFMAs.
 //   * Buffer loads clip at the end of each (batch, head) slice, so rows past Nq
 //     or Nk read as zeros without branches.
-//   * Workgroups are numbered so that each XCD (own L2) receives a contiguous slice
-//     of the work list, ordered (batch, K/V head) major, query block from the
-//     last (most keys under a causal mask) to the first, query heads of the GQA
-//     group minor: workgroups sharing K/V run together on one XCD.
+//   * Workgroups find their work from the XCD they run on (each XCD has its own
+//     L2): an XCD owns whole (batch, K/V head) groups where they divide over the
+//     XCDs, runs them from the last query block (most keys under a causal mask) to
+//     the first with the GQA group's query heads adjacent, so workgroups sharing
+//     K/V run together on one XCD; otherwise the bundles are dealt out in a snake
+//     so every XCD gets equal work (xcd_work).
 //   * Causal: key blocks wholly in the future of the workgroup's rows are never
 //     visited; only blocks crossing the diagonal or the ragged end are masked.
 #include <type_traits>
