@@ -98,9 +98,10 @@ int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse
                hipStream_t stream);
 
 /*
- * fa_forward_f32 — the same contract with fp32 Q, K, V.  Everything, including
- * the probabilities multiplied into V, stays in fp32 (nothing is rounded to a
- * 16-bit type).
+ * fa_forward_f32 — the same contract with fp32 Q, K, V: the attention of [LLM-basics]
+ * ①-2 (scores, 1/sqrt(d_k) scaling, row softmax, weighted sum of V) computed with the
+ * tile loop of [FA-notes] §5.2.  Everything, including the probabilities multiplied
+ * into V, stays in fp32 (nothing is rounded to a 16-bit type).
  */
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
@@ -168,8 +169,10 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, float* o, flo
                       int v_row_stride, hipStream_t stream);
 
 /*
- * fa_backward_workspace_bytes — bytes of device workspace fa_backward needs: two fp32
- * vectors of B * Hq * Nq entries (D_i and LSE_i log2 e), each padded to 256 bytes.
+ * fa_backward_workspace_bytes — helper (no computation): bytes of device workspace
+ * fa_backward needs for the two per-row statistics of the backward pass that
+ * [FA-notes] §5.2 recomputes from the forward's outputs: two fp32 vectors of
+ * B * Hq * Nq entries (D_i and LSE_i log2 e), each padded to 256 bytes.
  * Returns 0 for non-positive sizes.
  */
 size_t fa_backward_workspace_bytes(int B, int Hq, int Nq);
@@ -206,10 +209,11 @@ int fa_backward(const void* q, const void* k, const void* v, const float* o, con
                 hipStream_t stream);
 
 /*
- * fa_decode_splitkv_workspace_bytes — bytes of device workspace that
- * fa_decode_splitkv needs for these sizes (per-piece partial outputs and
- * log-sum-exps in fp32, room for ceil(Nk_max / chunk) + 1 pieces per (b, query
- * head)).  Returns 0 for invalid sizes.
+ * fa_decode_splitkv_workspace_bytes — helper (no computation): bytes of device
+ * workspace that fa_decode_splitkv needs for these sizes, i.e. the per-piece partial
+ * results (O_p, lse_p) that the two-block merge of [FA-notes] §4 combines: fp32, with
+ * room for ceil(ceil(Nk_max / 64) / (chunk / 64)) + 1 pieces per (b, query head).
+ * Returns 0 for invalid sizes.
  */
 size_t fa_decode_splitkv_workspace_bytes(int B, int Hq, int Nk_max, int d, int chunk);
 
@@ -262,7 +266,7 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
 /*
  * fa_decode_paged — fa_decode_splitkv over a paged KV cache.
  *
- * [LLM-basics] §8 (PagedAttention): the cache is a pool of fixed-size pages and each
+ * [LLM-basics] ②-8 (PagedAttention): the cache is a pool of fixed-size pages and each
  * sequence has a block table that maps its logical page j (keys j*page_size ..
  * (j+1)*page_size - 1) to a physical page; sequences may share pages.  The step, the
  * work split and the merge are those of fa_decode_splitkv, with every 64-key step
@@ -289,7 +293,8 @@ int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                     float scale, int chunk, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
-/* fa_status_str — a static, human-readable string for a status code. */
+/* fa_status_str — helper (no computation, no page passage): a static, human-readable
+ * string for a status code; unknown codes give "unknown fa_status". */
 const char* fa_status_str(int status);
 
 #ifdef __cplusplus

@@ -2,8 +2,9 @@
 
 The C ABI is declared in ``include/fa.h``.  This module only marshals arguments:
 it checks what it needs to read sizes off torch tensors, allocates outputs and
-workspace with torch (device memory plumbing), passes raw device pointers and the
-current HIP stream, and turns a negative status into ``ValueError``.  Every step
+workspace with torch (device memory plumbing, allocated in the stream order of the
+stream the kernels run on), passes raw device pointers and that stream (default:
+torch's current stream), and turns a negative status into ``ValueError``.  Every step
 of the computation runs in the library's HIP kernels; there is no fallback path.
 
 Functions (same names as the C entry points):
@@ -97,11 +98,25 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
-def _stream(stream) -> Optional[int]:
+def _torch_stream(stream):
+    """The torch stream object for ``stream`` (None = the current stream; a raw
+    hipStream_t handle is wrapped without taking ownership)."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _empty(shape, dtype, device, ts):
+    """Uninitialised device memory allocated in the stream order of ``ts``, the stream
+    the kernels will run on: when the tensor is freed (a workspace when the call
+    returns), torch's caching allocator hands the block only to later work ordered
+    after the kernels on that stream."""
+    import torch
+    with torch.cuda.stream(ts):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _check_tensor(t, name, dtype, ndim):
@@ -129,16 +144,17 @@ def _forward(entry, q, k, v, scale, causal, o, lse, stream, dtype) -> Tuple:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    ts = _torch_stream(stream)
     if o is None:
-        o = torch.empty((B, Nq, Hq, d), dtype=torch.float32, device=q.device)
+        o = _empty((B, Nq, Hq, d), torch.float32, q.device, ts)
     if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq, Nq), torch.float32, q.device, ts)
     _check_tensor(o, "o", torch.float32, 4)
     _check_tensor(lse, "lse", torch.float32, 3)
     if tuple(o.shape) != (B, Nq, Hq, d) or tuple(lse.shape) != (B, Hq, Nq):
         raise ValueError("o / lse have the wrong shape")
     st = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
-               float(scale), 1 if causal else 0, _stream(stream))
+               float(scale), 1 if causal else 0, int(ts.cuda_stream))
     if st != FA_OK:
         raise FAError(st, entry.__name__)
     return o, lse
@@ -172,17 +188,18 @@ def fa_forward_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: fl
         raise ValueError(f"shape mismatch: q {tuple(q8.shape)} k {tuple(k8.shape)} v {tuple(v8.shape)}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    ts = _torch_stream(stream)
     if o is None:
-        o = torch.empty((B, Nq, Hq, d), dtype=torch.float32, device=q8.device)
+        o = _empty((B, Nq, Hq, d), torch.float32, q8.device, ts)
     if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q8.device)
+        lse = _empty((B, Hq, Nq), torch.float32, q8.device, ts)
     _check_tensor(o, "o", torch.float32, 4)
     _check_tensor(lse, "lse", torch.float32, 3)
     if tuple(o.shape) != (B, Nq, Hq, d) or tuple(lse.shape) != (B, Hq, Nq):
         raise ValueError("o / lse have the wrong shape")
     st = lib().fa_forward_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq,
                               Nk, d, float(scale), 1 if causal else 0, float(q_descale),
-                              float(k_descale), float(v_descale), _stream(stream))
+                              float(k_descale), float(v_descale), int(ts.cuda_stream))
     if st != FA_OK:
         raise FAError(st, "fa_forward_fp8")
     return o, lse
@@ -221,10 +238,11 @@ def fa_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                          f"v {tuple(v.shape)} cu {B + 1}/{cu_seqlens_k.shape[0]}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    ts = _torch_stream(stream)
     if o is None:
-        o = torch.empty((total_q, Hq, d), dtype=torch.float32, device=q.device)
+        o = _empty((total_q, Hq, d), torch.float32, q.device, ts)
     if lse is None:
-        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+        lse = _empty((Hq, total_q), torch.float32, q.device, ts)
     _check_tensor(o, "o", torch.float32, 3)
     _check_tensor(lse, "lse", torch.float32, 2)
     if tuple(o.shape) != (total_q, Hq, d) or tuple(lse.shape) != (Hq, total_q):
@@ -233,7 +251,7 @@ def fa_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                                  _ptr(cu_seqlens_k), B, Hq, Hkv, int(max_seqlen_q),
                                  int(max_seqlen_k), total_q,
                                  total_k, d, float(scale), 1 if causal else 0, q.stride(0),
-                                 k.stride(0), v.stride(0), _stream(stream))
+                                 k.stride(0), v.stride(0), int(ts.cuda_stream))
     if st != FA_OK:
         raise FAError(st, "fa_forward_varlen")
     return o, lse
@@ -259,23 +277,24 @@ def fa_backward(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bo
         raise ValueError("backward shape mismatch")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    ts = _torch_stream(stream)
     if dq is None:
-        dq = torch.empty((B, Nq, Hq, d), dtype=torch.float32, device=q.device)
+        dq = _empty((B, Nq, Hq, d), torch.float32, q.device, ts)
     if dk is None:
-        dk = torch.empty((B, Nk, Hkv, d), dtype=torch.float32, device=q.device)
+        dk = _empty((B, Nk, Hkv, d), torch.float32, q.device, ts)
     if dv is None:
-        dv = torch.empty((B, Nk, Hkv, d), dtype=torch.float32, device=q.device)
+        dv = _empty((B, Nk, Hkv, d), torch.float32, q.device, ts)
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _check_tensor(t, n, torch.float32, 4)
     if tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
         raise ValueError("dq / dk / dv have the wrong shape")
     need = fa_backward_workspace_bytes(B, Hq, Nq)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+        workspace = _empty((max(need, 1),), torch.uint8, q.device, ts)
     st = lib().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                            _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, d, float(scale),
                            1 if causal else 0, _ptr(workspace),
-                           int(workspace.numel() * workspace.element_size()), _stream(stream))
+                           int(workspace.numel() * workspace.element_size()), int(ts.cuda_stream))
     if st != FA_OK:
         raise FAError(st, "fa_backward")
     return dq, dk, dv
@@ -328,17 +347,18 @@ def fa_decode_splitkv(q, k_cache, v_cache, seqlens_k, scale: Optional[float] = N
         raise ValueError("decode shape mismatch")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    ts = _torch_stream(stream)
     if o is None:
-        o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        o = _empty((B, Hq, d), torch.float32, q.device, ts)
     if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), torch.float32, q.device, ts)
     need = fa_decode_splitkv_workspace_bytes(B, Hq, Nk_max, d, chunk)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+        workspace = _empty((max(need, 1),), torch.uint8, q.device, ts)
     st = lib().fa_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o),
                                  _ptr(lse), B, Hq, Hkv, Nk_max, d, float(scale), int(chunk),
                                  _ptr(workspace), int(workspace.numel() * workspace.element_size()),
-                                 _stream(stream))
+                                 int(ts.cuda_stream))
     if st != FA_OK:
         raise FAError(st, "fa_decode_splitkv")
     return o, lse
@@ -362,17 +382,18 @@ def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, scale: Optional
         raise ValueError("paged decode shape mismatch")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    ts = _torch_stream(stream)
     if o is None:
-        o = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        o = _empty((B, Hq, d), torch.float32, q.device, ts)
     if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), torch.float32, q.device, ts)
     need = fa_decode_splitkv_workspace_bytes(B, Hq, max_pages * page_size, d, chunk)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+        workspace = _empty((max(need, 1),), torch.uint8, q.device, ts)
     st = lib().fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                                _ptr(seqlens_k), _ptr(o), _ptr(lse), B, Hq, Hkv, num_pages,
                                page_size, max_pages, d, float(scale), int(chunk), _ptr(workspace),
-                               int(workspace.numel() * workspace.element_size()), _stream(stream))
+                               int(workspace.numel() * workspace.element_size()), int(ts.cuda_stream))
     if st != FA_OK:
         raise FAError(st, "fa_decode_paged")
     return o, lse

@@ -31,7 +31,6 @@ CFLAGS = [
     "-Wno-unused-function",
     # packed-fp32 VALU forms are kept out of the generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

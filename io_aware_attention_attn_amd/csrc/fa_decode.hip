@@ -34,6 +34,7 @@
 //     the score layout hands P to the product.
 //   * Buffer loads clip at the sequence length, so cache rows at or beyond it read
 //     as zeros (and get -inf scores): poisoned padding cannot leak in.
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -72,7 +73,7 @@ struct Pos {
   int page;  // paged caches: physical page holding the step's keys
 };
 
-// Paged KV cache ([LLM-basics] §8, PagedAttention): the keys of sequence b are kept in
+// Paged KV cache ([LLM-basics] ②-8, PagedAttention): the keys of sequence b are kept in
 // pages of page_size keys, [num_pages, page_size, Hkv, d]; table[b * max_pages + j] is
 // the physical page of the sequence's logical page j.  page_size is a multiple of 64, so
 // a 64-key step never straddles two pages.  Unused by the contiguous-cache kernel.
@@ -545,17 +546,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   if (threadIdx.x == 0) LSE[row] = (nc > 0) ? Mtr + fast_log2(St) * kLn2 : kNegInf;
 }
 
+// Compute units of the current device, queried once per device and kept (the value
+// never changes while the process runs; racing first calls store the same number).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 template <int D, bool PAGED>
 hipError_t launch(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int QG = (G + 15) / 16;
   // Persistent wave workers: one workgroup (4 workers, 128 KB of LDS) per CU.
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-  }
+  const int cus = device_cus();
   const int rmin = a.chunk / kStep;  // a piece has at least `chunk` keys' worth of steps
   const Paging pg{a.block_table, a.max_pages, a.page_size, a.num_pages};
   hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)cus), dim3(kThreads), 0, s,

@@ -28,7 +28,8 @@ from .attention import (  # noqa: F401
     decode_attention,
     decode_attention_paged,
     lse_merge,
-    online_softmax_update,
+    block_state,
+    merge_states,
     online_attention_rows,
     safe_softmax,
     visible,

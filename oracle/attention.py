@@ -11,7 +11,6 @@ softmax are independent, so a row block is still the standard algorithm).
 """
 from __future__ import annotations
 
-import math
 from typing import Iterable, List, Optional, Sequence, Tuple
 
 import torch
@@ -157,7 +156,7 @@ def decode_attention_paged(q, k_pages, v_pages, block_table, lengths, page_size:
                            batches: Optional[Iterable[int]] = None):
     """One decode step over a paged KV cache.
 
-    [LLM-basics] §8 (PagedAttention): the cache is kept in fixed-size physical
+    [LLM-basics] ②-8 (PagedAttention): the cache is kept in fixed-size physical
     blocks ("pages") and a per-sequence block table maps the sequence's logical
     block j -- its keys j*page_size .. (j+1)*page_size - 1 -- to a physical page;
     several sequences may point at the same page.  k_pages and v_pages are
@@ -293,46 +292,52 @@ def attention_backward(q, k, v, do, scale: float, causal: bool,
     return dq, dk, dv
 
 
-def online_softmax_update(m_prev: torch.Tensor, l_prev: torch.Tensor, acc_prev: torch.Tensor,
-                          s_block: torch.Tensor, v_block: torch.Tensor):
-    """One block step of the online softmax, per row.
+def block_state(s_block: torch.Tensor, v_block: torch.Tensor):
+    """The softmax state of one block of keys taken on its own, per row.
 
-    [FA-notes] §4 and [LLM-basics] ③-2: with the running maximum m_prev and
-    running sum l_prev, a new block of scores with maximum m_cur gives
-        m_new = max(m_prev, m_cur)
-        l_new = e^(m_prev - m_new) * l_prev + e^(m_cur - m_new) * l_cur,
-    where l_cur = sum exp(s_block - m_cur).  [FA-notes] §5.2 rescales the
-    unnormalised output the same way:
-        acc_new = e^(m_prev - m_new) * acc_prev + e^(m_cur - m_new) * exp(s_block - m_cur) V_block.
-    m_prev = -inf, l_prev = 0, acc_prev = 0 before the first block (the sketch
-    leaves these uninitialised; this is the reading that makes the first step
-    reduce to the block's own softmax numerator).  Rows are the leading axis.
+    A state is the triple (m, l, acc) of [FA-notes] §4: m the largest score of the
+    row in the block, l = sum_j exp(s_j - m) and acc = sum_j exp(s_j - m) V_j (the
+    output before division by l).  Rows are the leading axis of ``s_block``.
     """
     s_block = _as64(s_block)
-    m_cur = torch.amax(s_block, dim=-1)
-    p_cur = torch.exp(s_block - m_cur.unsqueeze(-1))
-    l_cur = torch.sum(p_cur, dim=-1)
-    m_new = torch.maximum(m_prev, m_cur)
-    alpha = torch.exp(m_prev - m_new)
-    beta = torch.exp(m_cur - m_new)
-    l_new = alpha * l_prev + beta * l_cur
-    acc_new = alpha.unsqueeze(-1) * acc_prev + (beta.unsqueeze(-1) * p_cur) @ _as64(v_block)
-    return m_new, l_new, acc_new
+    m = torch.amax(s_block, dim=-1)
+    w = torch.exp(s_block - m.unsqueeze(-1))
+    return m, torch.sum(w, dim=-1), w @ _as64(v_block)
+
+
+def merge_states(first, second):
+    """Combine the softmax states of two disjoint key blocks of the same rows.
+
+    [FA-notes] §4 and [LLM-basics] ③-2: with the larger of the two maxima as the
+    common reference, m = max(m1, m2), each block's sum is brought to that
+    reference by the factor e^(m_i - m) and the two are added,
+        l = e^(m1 - m) l1 + e^(m2 - m) l2;
+    the unnormalised outputs take the same factors ([FA-notes] §5.2 rescales its
+    output accumulator the same way),
+        acc = e^(m1 - m) acc1 + e^(m2 - m) acc2.
+    The merge is symmetric in its two arguments.
+    """
+    m1, l1, acc1 = first
+    m2, l2, acc2 = second
+    m = torch.maximum(m1, m2)
+    f1 = torch.exp(m1 - m)
+    f2 = torch.exp(m2 - m)
+    return m, f1 * l1 + f2 * l2, f1.unsqueeze(-1) * acc1 + f2.unsqueeze(-1) * acc2
 
 
 def online_attention_rows(s: torch.Tensor, v: torch.Tensor, block_edges: List[int]):
     """Attention of score rows s [R, N] with values v [N, dv], consuming the keys in the
     contiguous blocks [e0, e1), [e1, e2), ... given by ``block_edges`` (e0 = 0,
-    last = N), via ``online_softmax_update``; the final output is acc / l
-    ([FA-notes] §5.2: P = exp(S - m) / l).  Returns (O, LSE) with LSE = m + ln l.
+    last = N): the state of the keys seen so far is merged with each new block's
+    state (``merge_states``), and the final output is acc / l ([FA-notes] §5.2:
+    P = exp(S - m) / l).  Returns (O, LSE) with LSE = m + ln l.
     """
     s, v = _as64(s), _as64(v)
-    R = s.shape[0]
-    m = torch.full((R,), float("-inf"), dtype=f64)
-    l = torch.zeros((R,), dtype=f64)
-    acc = torch.zeros((R, v.shape[1]), dtype=f64)
-    for a, e in zip(block_edges[:-1], block_edges[1:]):
-        m, l, acc = online_softmax_update(m, l, acc, s[:, a:e], v[a:e])
+    blocks = list(zip(block_edges[:-1], block_edges[1:]))
+    state = block_state(s[:, blocks[0][0]:blocks[0][1]], v[blocks[0][0]:blocks[0][1]])
+    for a, e in blocks[1:]:
+        state = merge_states(state, block_state(s[:, a:e], v[a:e]))
+    m, l, acc = state
     return acc / l.unsqueeze(-1), m + torch.log(l)
 
 
@@ -352,9 +357,3 @@ def lse_merge(o_parts, lse_parts) -> Tuple[torch.Tensor, torch.Tensor]:
     wn = torch.exp(lse_parts - lse)
     o = torch.sum(wn.unsqueeze(-1) * o_parts, dim=0)
     return o, lse
-
-
-def log_sum_exp_scalar(xs: Sequence[float]) -> float:
-    """ln sum_i e^{x_i} for a short Python list (used by the brute-force pins)."""
-    m = max(xs)
-    return m + math.log(sum(math.exp(x - m) for x in xs))

@@ -292,16 +292,23 @@ def pin_online_merge_bruteforce(orc):
             o, lse = orc.online_attention_rows(s, v, edges)
             _close(o, o_ref, 1e-14, f"online O n={n} edges={edges}")
             _close(lse, lse_ref, 1e-14, f"online LSE n={n} edges={edges}")
-    # a single update step reproduces the pages' two-block formulas on scalars
-    m1, l1, m2 = 1.5, 2.0, 3.0
+    # one merge reproduces the two-block formulas on scalars: a state (m1, l1, acc1) stated
+    # directly, and the state of a two-key block [3, 2] with V = (1, 10)
+    m1, l1, a1 = 1.5, 2.0, 0.25
     x2 = torch.tensor([[3.0, 2.0]], dtype=f64)
-    l2 = math.exp(0.0) + math.exp(-1.0)
-    m, l, acc = orc.online_softmax_update(torch.tensor([m1], dtype=f64), torch.tensor([l1], dtype=f64),
-                                          torch.zeros((1, 1), dtype=f64), x2,
-                                          torch.ones((2, 1), dtype=f64))
-    _close(m, [3.0], 0.0, "m_new = max(m1, m2)")
-    _close(l, [math.exp(m1 - 3.0) * l1 + math.exp(m2 - 3.0) * l2], 1e-15, "l_new")
-    _close(acc, [[l2]], 1e-15, "acc with V = 1 equals the block's exp sum")
+    vals = torch.tensor([[1.0], [10.0]], dtype=f64)
+    m2, l2, a2 = 3.0, 1.0 + math.exp(-1.0), 1.0 + 10.0 * math.exp(-1.0)
+    bm, bl, bacc = orc.block_state(x2, vals)
+    _close(bm, [m2], 0.0, "block max")
+    _close(bl, [l2], 1e-15, "block sum")
+    _close(bacc, [[a2]], 1e-15, "block numerator")
+    first = (torch.tensor([m1], dtype=f64), torch.tensor([l1], dtype=f64),
+             torch.tensor([[a1]], dtype=f64))
+    for order in ((first, (bm, bl, bacc)), ((bm, bl, bacc), first)):
+        m, l, acc = orc.merge_states(*order)
+        _close(m, [3.0], 0.0, "m_new = max(m1, m2)")
+        _close(l, [math.exp(m1 - 3.0) * l1 + math.exp(m2 - 3.0) * l2], 1e-15, "l_new")
+        _close(acc, [[math.exp(m1 - 3.0) * a1 + a2]], 1e-15, "acc_new")
 
 
 def pin_lse_merge_decode(orc):
@@ -352,7 +359,7 @@ def _paged_pool(num_pages, page_size, Hkv, d):
 
 
 def pin_paged_constant_pages(orc):
-    """[LLM-basics] §8: logical block j of a sequence lives in the physical page its
+    """[LLM-basics] ②-8: logical block j of a sequence lives in the physical page its
     block table names.  With K = 0 every valid key has score 0, so each query head's
     output is the plain mean of the valid V rows and LSE = ln L.  Every physical page
     holds one constant V row value, so the mean is the page constants weighted by how

@@ -294,3 +294,66 @@ def test_kv_cache_empty_layout(shape):
     assert delta % 16 == 0                      # V keeps K's 16-byte alignment
     assert delta % 1024 == fa.KV_V_OFFSET_MOD_1K == 256
     assert delta - nbytes < 1024                # at most one KiB of padding
+
+
+def test_binding_allocates_on_the_launch_stream(monkeypatch):
+    """Every tensor a wrapper allocates (outputs, workspace) is allocated in the stream
+    order of the stream the library is handed, not torch's current stream: a workspace
+    freed on return is then only reused by work ordered after the kernels.  Checked on
+    the CPU with the library and the stream replaced by recorders."""
+    torch = pytest.importorskip("torch")
+
+    class FakeStream:
+        cuda_stream = 0x5150
+
+    seen_alloc, seen_launch = [], []
+
+    def fake_empty(shape, dtype, device, ts):
+        seen_alloc.append(ts)
+        return torch.zeros(shape, dtype=dtype)
+
+    class FakeLib:
+        def __getattr__(self, name):
+            if name.endswith("_workspace_bytes"):
+                return lambda *a: 4096
+            if name == "fa_status_str":
+                return lambda st: b"x"
+
+            def entry(*args):
+                seen_launch.append(args[-1])
+                return 0
+            entry.__name__ = name
+            return entry
+
+    def no_direct_alloc(*a, **k):
+        raise AssertionError("wrapper allocated outside the launch stream")
+
+    monkeypatch.setattr(fa, "_torch_stream", lambda s: FakeStream())
+    monkeypatch.setattr(fa, "_empty", fake_empty)
+    monkeypatch.setattr(fa, "lib", lambda: FakeLib())
+    monkeypatch.setattr(fa, "_check_tensor", lambda *a, **k: None)
+    monkeypatch.setattr(fa, "_check_token_rows", lambda *a, **k: None)
+    monkeypatch.setattr(torch, "empty", no_direct_alloc)
+    bf = torch.bfloat16
+    q = torch.zeros((1, 4, 2, 64), dtype=bf)
+    k = torch.zeros((1, 4, 1, 64), dtype=bf)
+    o32 = torch.zeros((1, 4, 2, 64))
+    l32 = torch.zeros((1, 2, 4))
+    calls = [
+        lambda: fa.fa_forward(q, k, k, causal=True),
+        lambda: fa.fa_forward_f32(q.float(), k.float(), k.float()),
+        lambda: fa.fa_forward_fp8(q, k, k, 1.0, 1.0, 1.0),
+        lambda: fa.fa_forward_varlen(q[0], k[0], k[0], torch.tensor([0, 4], dtype=torch.int32),
+                                     torch.tensor([0, 4], dtype=torch.int32), 4, 4),
+        lambda: fa.fa_backward(q, k, k, o32, l32, q, causal=True),
+        lambda: fa.fa_decode_splitkv(q[:, 0], k, k, torch.tensor([4], dtype=torch.int32)),
+        lambda: fa.fa_decode_paged(q[:, 0], k, k, torch.zeros((1, 1), dtype=torch.int32),
+                                   torch.tensor([4], dtype=torch.int32)),
+    ]
+    for i, call in enumerate(calls):
+        seen_alloc.clear()
+        seen_launch.clear()
+        call()
+        assert seen_alloc, f"call {i} allocated nothing"
+        assert all(isinstance(t, FakeStream) for t in seen_alloc), i
+        assert seen_launch == [FakeStream.cuda_stream], i

@@ -31,9 +31,11 @@ MUTANTS = {
     "no max shift in attention": ("ex = torch.exp(s - m)\n                l = ", "ex = torch.exp(s)\n                l = "),
     "bwd no max shift": ("ex = torch.exp(s - m)\n                    p = ", "ex = torch.exp(s)\n                    p = "),
     "softmax without max shift": ("e = torch.exp(x - m)", "e = torch.exp(x)"),
-    "alpha sign": ("alpha = torch.exp(m_prev - m_new)", "alpha = torch.exp(m_new - m_prev)"),
-    "beta dropped on acc": ("(beta.unsqueeze(-1) * p_cur) @", "(p_cur) @"),
-    "l_new misses beta": ("l_new = alpha * l_prev + beta * l_cur", "l_new = alpha * l_prev + l_cur"),
+    "merge factor sign": ("f1 = torch.exp(m1 - m)", "f1 = torch.exp(m - m1)"),
+    "merge drops the second factor on acc": ("f2.unsqueeze(-1) * acc2", "acc2"),
+    "merge drops the second factor on l": ("f1 * l1 + f2 * l2", "f1 * l1 + l2"),
+    "merge keeps the first max": ("m = torch.maximum(m1, m2)", "m = m1"),
+    "block sum without max shift": ("w = torch.exp(s_block - m.unsqueeze(-1))", "w = torch.exp(s_block)"),
     "merge weight vs M": ("wn = torch.exp(lse_parts - lse)", "wn = torch.exp(lse_parts - M)"),
     "final O not normalised": ("return acc / l.unsqueeze(-1), m + torch.log(l)",
                                "return acc, m + torch.log(l)"),

@@ -293,7 +293,7 @@ def test_decode_empty_sequences():
 
 
 # ---------------------------------------------------------------------------
-# paged KV-cache decode ([LLM-basics] §8, PagedAttention)
+# paged KV-cache decode ([LLM-basics] ②-8, PagedAttention)
 # ---------------------------------------------------------------------------
 
 def _run_paged(q, kp, vp, table, lengths, scale, chunk):

@@ -87,3 +87,35 @@ def test_decode_paged_streams():
     kp, vp, table = W.paged_from_contiguous(kc, vc, lengths, 128, seed=38, spare_pages=3)
     q, kp, vp, table, ld = q.to(dev), kp.to(dev), vp.to(dev), table.to(dev), lengths.to(dev)
     _three_runs(lambda s: fa.fa_decode_paged(q, kp, vp, table, ld, chunk=128, stream=s))
+
+
+def test_stream_argument_without_making_it_current():
+    """stream=s while torch's current stream stays the default one.  A long prefill is
+    queued on s first, so the decode and backward queued behind it run well after the
+    wrappers return and free their workspaces; the current stream meanwhile allocates
+    blocks of the same sizes and fills them with NaN.  The workspaces were allocated in
+    s's stream order, so those blocks are not the ones the kernels still read, and the
+    results equal the same calls made on the current stream."""
+    dev = _dev()
+    lengths, q, kc, vc = W.decode_inputs(4, 16, 2, 128, 3000, 1, 3000, seed=39)
+    q, kc, vc, ld = q.to(dev), kc.to(dev), vc.to(dev), lengths.to(dev)
+    qb, kb, vb, dob = (t.to(dev) for t in W.backward_inputs(1, 4, 2, 300, 300, 64, seed=40))
+    ob, lb = fa.fa_forward(qb, kb, vb, causal=True)
+    ref_dec = [t.clone() for t in fa.fa_decode_splitkv(q, kc, vc, ld, chunk=256)]
+    ref_bwd = [t.clone() for t in fa.fa_backward(qb, kb, vb, ob, lb, dob, causal=True)]
+    qp, kp, vp = (t.to(dev) for t in W.prefill_inputs(1, 32, 4, 8192, 8192, 128, seed=41))
+    torch.cuda.synchronize()
+    ws_dec = fa.fa_decode_splitkv_workspace_bytes(4, 16, 3000, 128, 256)
+    ws_bwd = fa.fa_backward_workspace_bytes(1, 4, 300)
+    s = torch.cuda.Stream()
+    assert torch.cuda.current_stream() != s
+    for _ in range(3):
+        fa.fa_forward(qp, kp, vp, causal=True, stream=s)  # keeps s busy for ~1.5 ms
+        dec = fa.fa_decode_splitkv(q, kc, vc, ld, chunk=256, stream=s)
+        bwd = fa.fa_backward(qb, kb, vb, ob, lb, dob, causal=True, stream=s)
+        junk = [torch.full((n,), 255, dtype=torch.uint8, device=dev) for n in (ws_dec, ws_bwd)]
+        s.synchronize()
+        torch.cuda.synchronize()
+        del junk
+        for x, y in zip(ref_dec + ref_bwd, list(dec) + list(bwd)):
+            assert torch.equal(x, y), "result changed when the stream was not current"
