@@ -22,8 +22,10 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers, contiguous, row-major, 16-byte
- *     aligned (the decode LSE output and seqlens_k need only 4-byte alignment).  The caller owns every buffer; the library allocates nothing,
- *     keeps no state and never synchronises.  Work is enqueued on `stream`
+ *     aligned (the decode LSE output and seqlens_k need only 4-byte alignment).  The
+ *     caller owns every buffer; the library allocates nothing and never synchronises.
+ *     Its only state is a fixed device scratch array (one per GPU, held until the
+ *     process ends) used by fa_decode_splitkv_noalloc.  Work is enqueued on `stream`
  *     (NULL = the default stream) and the call returns right after the launch.
  *   - Arguments are validated on the host before any HIP call; a negative
  *     fa_status is returned and nothing is launched.  A launch failure reported
@@ -68,7 +70,9 @@ typedef enum {
   FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned (or a packed row
                               stride is not a multiple of 8 elements) */
   FA_ERR_WORKSPACE = -5,   /* decode or backward workspace missing or smaller than required */
-  FA_ERR_HIP = -6          /* the kernel launch failed (hipGetLastError) */
+  FA_ERR_HIP = -6,         /* the kernel launch failed (hipGetLastError) */
+  FA_ERR_SCRATCH = -7      /* fa_decode_splitkv_noalloc: the request needs more than the
+                              library's fixed device scratch */
 } fa_status;
 
 /*
@@ -262,6 +266,29 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       const int* seqlens_k, float* o, float* lse,
                       int B, int Hq, int Hkv, int Nk_max, int d, float scale, int chunk,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_decode_splitkv_noalloc — fa_decode_splitkv for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, computation, results (bit for bit) and errors as
+ * fa_decode_splitkv, without the workspace: the split kernel's partial results go to a
+ * device scratch array of the library, 80 MiB per GPU (a file-scope device array, so
+ * every GPU the library runs on holds its own copy until the process ends).  The call
+ * allocates nothing (no hipMalloc / hipFree or allocating library routine).
+ *   - A request whose partial results need more than 80 MiB, i.e. more than
+ *     fa_decode_splitkv_workspace_bytes(B, Hq, Nk_max, d, chunk) reports, returns
+ *     FA_ERR_SCRATCH before any HIP call (the 16-sequence, 64-query-head, d = 128,
+ *     Nk_max = 32768, chunk = 256 decode needs 68.2 MB).
+ *   - Every call on one GPU uses that GPU's one scratch array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero).  Calls that overlap in
+ *     time on one GPU (two streams, two host threads without ordering) race on it and
+ *     give undefined results; calls ordered on one stream are safe.
+ *   - The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress) with that device current; FA_ERR_HIP if that fails.
+ */
+int fa_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int* seqlens_k, float* o, float* lse, int B, int Hq, int Hkv,
+                              int Nk_max, int d, float scale, int chunk, hipStream_t stream);
 
 /*
  * fa_decode_paged — fa_decode_splitkv over a paged KV cache.

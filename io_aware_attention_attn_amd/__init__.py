@@ -20,6 +20,8 @@ Functions (same names as the C entry points):
   fa_decode_splitkv_workspace_bytes(B, Hq, Nk_max, d, chunk=256)
   fa_decode_splitkv(q, k_cache, v_cache, seqlens_k, scale=None, chunk=256, o=None,
                     lse=None, workspace=None, stream=None)
+  fa_decode_splitkv_noalloc(q, k_cache, v_cache, seqlens_k, scale=None, chunk=256, o, lse,
+                            stream=None)
   fa_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, scale=None, chunk=256,
                   o=None, lse=None, workspace=None, stream=None)
   fa_status_str(status)
@@ -44,6 +46,7 @@ FA_ERR_UNSUPPORTED = -3
 FA_ERR_ALIGN = -4
 FA_ERR_WORKSPACE = -5
 FA_ERR_HIP = -6
+FA_ERR_SCRATCH = -7
 
 _lib = None
 
@@ -82,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_splitkv_workspace_bytes.restype = sz
     L.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     L.fa_decode_splitkv.restype = i
+    L.fa_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.fa_decode_splitkv_noalloc.restype = i
     L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.fa_decode_paged.restype = i
     L.fa_status_str.argtypes = [i]
@@ -361,6 +366,34 @@ def fa_decode_splitkv(q, k_cache, v_cache, seqlens_k, scale: Optional[float] = N
                                  int(ts.cuda_stream))
     if st != FA_OK:
         raise FAError(st, "fa_decode_splitkv")
+    return o, lse
+
+
+def fa_decode_splitkv_noalloc(q, k_cache, v_cache, seqlens_k, o, lse,
+                              scale: Optional[float] = None, chunk: int = 256, stream=None):
+    """fa_decode_splitkv without a workspace: the library's fixed per-GPU device scratch
+    holds the partial results, and nothing is allocated (the caller passes o fp32 [B,Hq,d]
+    and lse fp32 [B,Hq]).  Calls that overlap in time on one GPU race on that scratch.
+    Raises FAError (FA_ERR_SCRATCH) when the request does not fit it."""
+    import torch
+    _check_tensor(q, "q", torch.bfloat16, 3)
+    _check_tensor(k_cache, "k_cache", torch.bfloat16, 4)
+    _check_tensor(v_cache, "v_cache", torch.bfloat16, 4)
+    _check_tensor(seqlens_k, "seqlens_k", torch.int32, 1)
+    _check_tensor(o, "o", torch.float32, 3)
+    _check_tensor(lse, "lse", torch.float32, 2)
+    B, Hq, d = q.shape
+    Bc, Nk_max, Hkv, dc = k_cache.shape
+    if (tuple(v_cache.shape) != tuple(k_cache.shape) or Bc != B or dc != d
+            or seqlens_k.shape[0] != B or tuple(o.shape) != (B, Hq, d) or tuple(lse.shape) != (B, Hq)):
+        raise ValueError("decode shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_decode_splitkv_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k),
+                                         _ptr(o), _ptr(lse), B, Hq, Hkv, Nk_max, d, float(scale),
+                                         int(chunk), int(_torch_stream(stream).cuda_stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_splitkv_noalloc")
     return o, lse
 
 

@@ -1,10 +1,14 @@
 // fa_api.hip — the C ABI declared in include/fa.h: host-side validation, kernel
 // selection and launch.  Validation happens before any HIP call; nothing here
-// allocates, synchronises or keeps state.
+// allocates or synchronises.  The only state is the per-device address of the fixed
+// scratch array that fa_decode_splitkv_noalloc uses in place of a workspace.
 #include "fa.h"
 
 #include <limits.h>
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "fa_internal.h"
 
@@ -51,6 +55,64 @@ int check_decode_sizes(int B, int Hq, int Hkv, int Nk_max, int d, int chunk) {
   const long long steps = (long long)B * Hq * ((Nk_max + 63) / 64);
   if (steps > 0x3fffffffLL || Hq > 65535 || B > 65535) return FA_ERR_SHAPE;
   return FA_OK;
+}
+
+// Validation shared by the two contiguous-cache decode entry points (everything but
+// the workspace).
+int check_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                         const int* seqlens_k, const float* o, const float* lse, int B, int Hq,
+                         int Hkv, int Nk_max, int d, int chunk) {
+  if (!q || !k_cache || !v_cache || !seqlens_k || !o || !lse) return FA_ERR_NULL;
+  const int st = check_decode_sizes(B, Hq, Hkv, Nk_max, d, chunk);
+  if (st != FA_OK) return st;
+  // one sequence's K or V rows are addressed with 32-bit byte offsets
+  if ((long long)(Nk_max + 64) * Hkv * d * 2 > INT_MAX) return FA_ERR_SHAPE;
+  if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(o) ||
+      (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+// Split + merge kernels of a contiguous-cache decode with the partial results in
+// `workspace` (large enough, 16-byte aligned: checked by the callers).
+int launch_decode_contiguous(const void* q, const void* k_cache, const void* v_cache,
+                             const int* seqlens_k, float* o, float* lse, int B, int Hq, int Hkv,
+                             int Nk_max, int d, float scale, int chunk, void* workspace,
+                             hipStream_t stream) {
+  const int mp = max_pieces_of(Nk_max, chunk);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             fa::decode_part_o_bytes(B, Hq, mp, d));
+  fa::DecodeArgs a{q, k_cache, v_cache, seqlens_k, o, lse, part_o, part_lse,
+                   B, Hq, Hkv, Nk_max, d, chunk, mp, scale};
+  return fa::launch_decode_splitkv(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// Device scratch of fa_decode_splitkv_noalloc: the split kernel's partial results live
+// here instead of in a caller workspace.  Every GPU the library runs on holds its own
+// copy of the array (at its own address) until the process ends.  In host code the
+// name `scratch` is only a host-side stand-in for the symbol, never a device address;
+// the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)80 << 20;  // 80 MiB
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of the current device's copy of `scratch` (looked up on the first call
+// on that device, with that device current, and kept), or nullptr if the lookup fails.
+void* scratch_of_current_device() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = ptrs[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  return p;
 }
 
 }  // namespace
@@ -159,24 +221,30 @@ int fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                       const int* seqlens_k, float* o, float* lse, int B, int Hq, int Hkv,
                       int Nk_max, int d, float scale, int chunk, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k_cache || !v_cache || !seqlens_k || !o || !lse) return FA_ERR_NULL;
-  const int st = check_decode_sizes(B, Hq, Hkv, Nk_max, d, chunk);
+  const int st = check_decode_splitkv(q, k_cache, v_cache, seqlens_k, o, lse, B, Hq, Hkv, Nk_max,
+                                      d, chunk);
   if (st != FA_OK) return st;
-  // one sequence's K or V rows are addressed with 32-bit byte offsets
-  if ((long long)(Nk_max + 64) * Hkv * d * 2 > INT_MAX) return FA_ERR_SHAPE;
-  if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(o) ||
-      (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u))
-    return FA_ERR_ALIGN;
   const int mp = max_pieces_of(Nk_max, chunk);
   const size_t need = fa::decode_part_o_bytes(B, Hq, mp, d) + fa::decode_part_lse_bytes(B, Hq, mp);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (misaligned(workspace)) return FA_ERR_ALIGN;
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             fa::decode_part_o_bytes(B, Hq, mp, d));
-  fa::DecodeArgs a{q, k_cache, v_cache, seqlens_k, o, lse, part_o, part_lse,
-                   B, Hq, Hkv, Nk_max, d, chunk, mp, scale};
-  return fa::launch_decode_splitkv(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return launch_decode_contiguous(q, k_cache, v_cache, seqlens_k, o, lse, B, Hq, Hkv, Nk_max, d,
+                                  scale, chunk, workspace, stream);
+}
+
+int fa_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int* seqlens_k, float* o, float* lse, int B, int Hq, int Hkv,
+                              int Nk_max, int d, float scale, int chunk, hipStream_t stream) {
+  const int st = check_decode_splitkv(q, k_cache, v_cache, seqlens_k, o, lse, B, Hq, Hkv, Nk_max,
+                                      d, chunk);
+  if (st != FA_OK) return st;
+  const int mp = max_pieces_of(Nk_max, chunk);
+  const size_t need = fa::decode_part_o_bytes(B, Hq, mp, d) + fa::decode_part_lse_bytes(B, Hq, mp);
+  if (need > kScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = scratch_of_current_device();
+  if (ws == nullptr) return FA_ERR_HIP;
+  return launch_decode_contiguous(q, k_cache, v_cache, seqlens_k, o, lse, B, Hq, Hkv, Nk_max, d,
+                                  scale, chunk, ws, stream);
 }
 
 int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -227,6 +295,9 @@ const char* fa_status_str(int status) {
                               "packed row stride is not a multiple of 8 elements)";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: the decode's partial results would not fit the "
+                                "library's fixed 80 MiB device scratch (fa_decode_splitkv_noalloc); "
+                                "use fa_decode_splitkv with a workspace";
     default: return "unknown fa_status";
   }
 }

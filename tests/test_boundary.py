@@ -38,13 +38,14 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"fa_forward", "fa_forward_f32", "fa_forward_fp8", "fa_forward_varlen",
                           "fa_backward_workspace_bytes", "fa_backward",
                           "fa_decode_splitkv_workspace_bytes",
-                          "fa_decode_splitkv", "fa_decode_paged", "fa_status_str"}
+                          "fa_decode_splitkv", "fa_decode_splitkv_noalloc", "fa_decode_paged",
+                          "fa_status_str"}
     for n in names:
         assert hasattr(L, n), f"libfa.so does not export {n}"
 
 
 def test_status_strings(L):
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         s = fa.fa_status_str(st)
         assert s.startswith("FA_"), s
     assert "unknown" in fa.fa_status_str(-99)
@@ -220,6 +221,45 @@ def _dec(L, q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nk_max=512, d=1
 ])
 def test_decode_rejects(L, kw, status):
     assert _dec(L, **kw) == status
+
+
+def _dec_noalloc(L, q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Nk_max=512, d=128,
+                 scale=0.1, chunk=256):
+    return L.fa_decode_splitkv_noalloc(q, kc, vc, sl, o, lse, B, Hq, Hkv, Nk_max, d, scale, chunk,
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_NULL),
+    (dict(vc=None), fa.FA_ERR_NULL),
+    (dict(o=None), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_SHAPE),
+    (dict(B=1, Hq=8, Hkv=8, Nk_max=1048513), fa.FA_ERR_SHAPE),
+    (dict(d=100), fa.FA_ERR_UNSUPPORTED),
+    (dict(chunk=100), fa.FA_ERR_UNSUPPORTED),
+    (dict(lse=0x10001), fa.FA_ERR_ALIGN),
+    (dict(vc=MIS), fa.FA_ERR_ALIGN),
+    # partial results beyond the 80 MiB scratch: 64 heads at 32768 keys and chunk 256 need
+    # 4.26 MB per sequence (129 pieces x (128 + 1) floats per head), so 20 sequences do not
+    # fit; with chunk 64 (513 pieces) 5 sequences do not
+    (dict(B=20, Hq=64, Hkv=8, Nk_max=32768), fa.FA_ERR_SCRATCH),
+    (dict(B=5, Hq=64, Hkv=8, Nk_max=32768, chunk=64), fa.FA_ERR_SCRATCH),
+])
+def test_decode_noalloc_rejects(L, kw, status):
+    """Invalid requests, and requests larger than the fixed scratch, are refused before any
+    HIP call (so also here, without a GPU)."""
+    assert _dec_noalloc(L, **kw) == status
+
+
+def test_decode_noalloc_scratch_limit_matches_workspace_query():
+    """The scratch limit is stated in workspace bytes: the largest accepted requests are
+    those whose fa_decode_splitkv workspace fits 80 MiB."""
+    limit = 80 << 20
+    assert fa.fa_decode_splitkv_workspace_bytes(16, 64, 32768, 128, 256) <= limit
+    assert fa.fa_decode_splitkv_workspace_bytes(19, 64, 32768, 128, 256) <= limit
+    assert fa.fa_decode_splitkv_workspace_bytes(20, 64, 32768, 128, 256) > limit
+    assert fa.fa_decode_splitkv_workspace_bytes(5, 64, 32768, 128, 64) > limit
 
 
 def _paged(L, q=P, kp=P, vp=P, bt=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, num_pages=16,
