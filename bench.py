@@ -12,9 +12,12 @@ One step = one pass of the whole hot path on resident synthetic inputs:
 `value` is the prefill's algorithmic TFLOP/s (4*B*Hq*Nq*Nk*d / 2 for causal) over
 its measured kernel time; the decode's HBM GB/s (compulsory K/V/q/O/LSE bytes)
 is reported alongside, and so are the paged-KV decode, the packed variable-length
-prefill (16 causal GQA sequences, lengths ~U[512, 16384], one launch), the FP8 forward
-and the backward pass on the prefill workload's shape, each timed on its own after the
-step.  Kernel times come from HIP events recorded on the
+prefill (16 causal GQA sequences, lengths ~U[512, 16384], one launch), the FP8 forward,
+the backward pass on the prefill workload's shape, and the two other prefill workloads (the
+peaky causal MHA one, B=1 H=32 N=8192 d=128 with Q, K x1.5, and the short causal MHA one,
+B=2 H=12 N=2048 d=64, each with its own roofline fraction), each timed on its own after the
+step.  The decode's reported rate is that of back-to-back decode calls; the same call timed
+inside the step (right after each 15 ms prefill) is reported beside it as `in_step`.  Kernel times come from HIP events recorded on the
 stream the kernels are launched on (torch's current stream), around every
 launch of the timed region.
 
@@ -47,6 +50,9 @@ def parse():
     ap.add_argument("--prefill", default="c4", choices=["c2", "c3", "c4"],
                     help="prefill workload (default: the long-context GQA one)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the other prefill workloads (short MHA and peaky 8K MHA), each "
+                         "timed on its own after the step")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-KV decode measurement (reported beside the step)")
     ap.add_argument("--no-varlen", action="store_true",
@@ -362,6 +368,82 @@ def bench_backward(fa, W, pcfg, dev, K):
             "kernels": "prep (D, lse2) + dK/dV per 128 keys + dQ per 128 rows (one call)"}
 
 
+def bench_prefill_leg(fa, W, name, dev, launches, min_seconds=0.3):
+    """Another prefill workload of the same kernel (the short MHA one, or the peaky 8K MHA
+    one), timed on its own after the step: `launches` back-to-back launches, each between
+    two HIP events on the stream the kernel runs on; algorithmic TFLOP/s as for the step."""
+    import torch
+    cfg = W.CONFIGS[name]
+    print(f"[bench] prefill leg {name}", file=sys.stderr, flush=True)
+    q, k, v = W.prefill_inputs_for(cfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty((cfg.B, cfg.Nq, cfg.Hq, cfg.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.Nq), dtype=torch.float32, device=dev)
+
+    def call():
+        fa.fa_forward(qd, kd, vd, scale=cfg.scale, causal=cfg.causal, o=o, lse=lse)
+    t0 = time.perf_counter()
+    n = 0
+    while n < 10 or time.perf_counter() - t0 < min_seconds:
+        call()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / launches
+    flops = cfg.flops()
+    tf = flops / (avg * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
+            "median_launch_ms": round(sorted(ms)[launches // 2], 4), "launches": launches,
+            "flop_per_launch": flops, "workload": cfg.workload,
+            "kernel": f"prefill_bf16_kernel<{cfg.d}, causal>"}
+
+
+def decode_piece_steps(lengths, dcfg, cus):
+    """The decode's real split: all (batch, K/V head, head group) segments laid end to end
+    in 64-key steps, T steps in all, cut into equal runs of R = max(ceil(T / W), chunk / 64)
+    steps over the W = 4 * CUs persistent waves (the rule the split kernel applies)."""
+    G = dcfg.Hq // dcfg.Hkv
+    QG = (G + 15) // 16
+    T = sum((int(L) + 63) // 64 for L in lengths) * dcfg.Hkv * QG
+    Wv = 4 * cus
+    R = max((T + Wv - 1) // Wv, dcfg.chunk // 64)
+    return T, Wv, R
+
+
+def bench_decode_isolated(fa, W, dcfg, dec, K):
+    """The step's decode call (caches from kv_cache_empty) timed on its own: K back-to-back
+    calls, each between two HIP events, with no prefill launched in between."""
+    import torch
+
+    def call():
+        fa.fa_decode_splitkv(dec["dq"], dec["dkc"], dec["dvc"], dec["dl"], scale=dcfg.scale,
+                             chunk=dcfg.chunk, o=dec["o"], lse=dec["lse"], workspace=dec["ws"])
+    print("[bench] decode, isolated", file=sys.stderr, flush=True)
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return sum(ms) / K, sorted(ms)[K // 2]
+
+
 def cpu_baseline_decode(cfg, lengths, q, kc, vc, target_s):
     import torch
     import oracle
@@ -485,7 +567,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs rounded to bf16; no dataset or weights)",
         "config": {"workload": pcfg.workload, "B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv,
                    "seq_len": pcfg.Nq, "head_dim": pcfg.d, "causal": pcfg.causal,
-                   "decode_workload": None if not dec else dcfg.workload,
+                   "decode_workload": None if not dec else dcfg.workload + " (minimum run; "
+                                     "real runs in decode.piece_keys)",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, causal>",
                      "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -499,18 +582,32 @@ def main():
         "wall_s_timed_region": round(wall, 3),
     }
     if dec:
-        dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
-        avg_dec = sum(dec_ms) / K
         dbytes = W.decode_bytes(dec["lengths"].tolist(), dcfg.Hq, dcfg.Hkv, dcfg.d)
-        gbs = dbytes / (avg_dec * 1e-3) / 1e9
+        dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
+        step_avg = sum(dec_ms) / K
+        step_gbs = dbytes / (step_avg * 1e-3) / 1e9
+        iso_avg, iso_med = bench_decode_isolated(fa, W, dcfg, dec, max(K, 50))
+        gbs = dbytes / (iso_avg * 1e-3) / 1e9
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        T, Wv, R = decode_piece_steps(dec["lengths"].tolist(), dcfg, cus)
         result["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
                             "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
-                            "avg_call_ms": round(avg_dec, 4),
-                            "median_call_ms": round(sorted(dec_ms)[K // 2], 4),
+                            "timing": f"{max(K, 50)} back-to-back decode calls, each between "
+                                      f"HIP events (in_step: the same call timed inside the "
+                                      f"step, right after each prefill)",
+                            "avg_call_ms": round(iso_avg, 4), "median_call_ms": round(iso_med, 4),
+                            "in_step": {"value": round(step_gbs, 1), "unit": "GB/s",
+                                        "frac": round(step_gbs / PEAK_HBM_GBS, 4),
+                                        "avg_call_ms": round(step_avg, 4),
+                                        "median_call_ms": round(sorted(dec_ms)[K // 2], 4)},
                             "kernels": "split + merge (one call)",
-                            "split": "key work of all (batch, K/V head) segments cut into equal "
-                                     "per-wave runs of 64-key steps, pieces of >= chunk keys; "
-                                     "LSE merge of the pieces",
+                            "split": f"key work of all (batch, K/V head) segments laid end to end "
+                                     f"in 64-key steps ({T} steps) and cut into equal runs of "
+                                     f"R = max(ceil(T / W), chunk / 64) = {R} steps ({64 * R} "
+                                     f"keys) over W = {Wv} persistent waves; a piece is a run's "
+                                     f"part inside one segment (>= chunk keys unless the segment "
+                                     f"is shorter); LSE merge of the pieces",
+                            "piece_steps": R, "piece_keys": 64 * R, "waves": Wv,
                             "bytes_per_call": dbytes,
                             "sum_seqlens": int(dec["lengths"].sum().item()),
                             "traffic_split": profiled_traffic("decode_split_kernel<128, false>"),
@@ -521,9 +618,18 @@ def main():
         result["decode"]["separate_allocations"] = bench_decode_separate(fa, W, dcfg, dec, dev, K)
     if dec and not args.no_paged:
         result["decode_paged"] = bench_paged(fa, W, dcfg, dec, dev, K)
-    if not args.no_varlen or not args.no_backward or not args.no_fp8:
+    if not args.no_varlen or not args.no_backward or not args.no_fp8 or not args.no_legs:
         del qd, kd, vd, o, lse
         torch.cuda.empty_cache()
+    if not args.no_legs:
+        # the other prefill workloads of the same kernel: the peaky 8K MHA one (N >= 8192,
+        # d = 128, the roofline target applies) and the short MHA one
+        legs = {}
+        for name, launches in (("c3", max(100, 5 * K)), ("c2", 1000)):
+            if name != pcfg.name:
+                legs[name] = bench_prefill_leg(fa, W, name, dev, launches)
+                torch.cuda.empty_cache()
+        result["prefill_legs"] = legs
     if not args.no_varlen:
         result["prefill_varlen"] = bench_varlen(fa, W, dev, K)
         torch.cuda.empty_cache()

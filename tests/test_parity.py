@@ -92,10 +92,16 @@ def _sampled(cfg, heads, row_blocks):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
-def test_c3_sampled():
+def test_c3_full():
+    """The peaky 8K causal MHA workload (Q, K x1.5: scores spread widely, so the exponent
+    reference moves often) compared on every element of O and LSE: the oracle's full
+    standard attention, row-blocked, on all 32 heads."""
     cfg = W.CONFIGS["c3"]
-    N = cfg.Nq
-    _sampled(cfg, heads=[0, 13, 31], row_blocks=[(0, 512), (4000, 4200), (N - 512, N)])
+    q, k, v = W.prefill_inputs_for(cfg)
+    o, lse = _run_forward(q, k, v, cfg.scale, cfg.causal)
+    print("[c3] GPU done, oracle running", flush=True)
+    o_ref, lse_ref = oracle.attention(q, k, v, cfg.scale, cfg.causal, row_block=2048)
+    _cmp(o.cpu(), lse.cpu(), o_ref, lse_ref, TOL_BF16, "c3 (every element)")
 
 
 def test_c4_sampled():
