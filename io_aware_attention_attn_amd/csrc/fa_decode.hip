@@ -22,11 +22,14 @@
 //     the length mix.  A wave writes one partial result (O_p, lse_p) for each piece of
 //     a segment that its range covers, so a segment of n steps has at most
 //     ceil(n / R) + 1 pieces and the merge reads a few records per query head.
-//   * Software pipeline over the wave's steps: while step s is computed, K of step
-//     s+1 is already in flight into a second VGPR set and V of step s+1 into the
-//     second half of the wave's LDS slice (buffer_load ... lds).
-//   * Scores S^T = K q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d straight
-//     from the K registers, B = the group's query heads (up to 16, zero-padded).
+//   * Software pipeline over the wave's steps: while step s is computed, the K and V
+//     rows of step s+1 are in flight into registers.  Each load instruction fetches
+//     whole head rows (4 rows x 256 bytes at d = 128): fetched 16 keys x 64 bytes per
+//     instruction, the layout the score product wants in registers, the same bytes
+//     stream about 9% slower.  A landed step is written to the wave's own LDS slice and
+//     the MFMA operands are read from there.
+//   * Scores S^T = K q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d read as rows
+//     from LDS, B = the group's query heads (up to 16, zero-padded).
 //     The matrix cores are far from busy; they are used because the group's query
 //     heads make the per-byte arithmetic too high for plain fp32 VALU at HBM speed.
 //   * O^T = V^T P^T with the same instruction; V^T comes from the row-major V slice
@@ -94,13 +97,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     float* __restrict__ part_lse, int B, int Hq, int Hkv, int Nk_max, int rmin, int max_pieces,
     int QG, float c, Paging pg) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
-  constexpr int VI = kStep * CH / 64;    // LDS-direct instructions per step
+  constexpr int RPI = 64 / CH;           // cache rows per load instruction (whole rows)
+  constexpr int NI = kStep / RPI;        // load instructions per step, K and V each (= CH)
   constexpr int DB = D / 16;             // 16-row d blocks of O^T
   constexpr int KS = D / 32;             // 32-wide d steps of the score product
-  // One array per stage: the compiler's wait insertion can then tell the LDS-DMA
-  // prefetch into one stage from the reads of the other and does not stall on it.
-  __shared__ __attribute__((aligned(1024))) uint16_t vst0[kWaves][kStep * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t vst1[kWaves][kStep * D];
+  // Each wave stages one step of K and of V in its own LDS slice (no barrier needed):
+  // the cache rows arrive in registers with whole 256-byte head rows per load instruction
+  // (the access pattern HBM serves fastest) and are written to LDS, from where the MFMA
+  // operands are read: K rows directly, V^T through transposed reads.
+  __shared__ __attribute__((aligned(1024))) uint16_t kst[kWaves][kStep * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vst[kWaves][kStep * D];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -110,17 +116,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
 
   // ---- per-lane fixed offsets
-  // K fragment (A of S^T): key 16*kb + l16 of the step, d = 32*st + 8*g.
-  const uint32_t k_lane = (uint32_t)l16 * row_bytes + 16u * g;
-  // V LDS-direct: instruction i covers rows (64*i + lane) / CH; the row offset part
-  // that grows with i goes in the scalar offset.
-  uint32_t v_lane[2];
+  // Loads: instruction i of a step covers rows RPI i .. RPI i + RPI - 1; lane -> row
+  // lane / CH, chunk lane % CH.
+  const int ld_row = lane / CH;
+  const int ld_chunk = lane % CH;
+  const uint32_t ld_off = (uint32_t)ld_row * row_bytes + (uint32_t)ld_chunk * 16u;
+  // LDS byte offsets the lane writes its chunk to (row RPI i + ld_row): K rows swizzled so
+  // the 16 rows of one K operand read fall in 16 different bank groups, V rows as the
+  // transposed reads need.  The swizzles depend on the row only through ld_row's low bits
+  // and RPI i, and RPI i is a multiple of 4 (D = 128) or 8 (D = 64).
+  uint32_t kw_off[NI], vw_off[NI];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int lin = e * 64 + lane;
-    const int row = lin / CH;
-    const int pos = lin % CH;
-    v_lane[e] = (uint32_t)row * row_bytes + (uint32_t)((pos ^ dswz<D>(row)) * 16);
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * i + ld_row;
+    const int ksw = D == 128 ? (row & 15) : ((row >> 1) & 7);
+    kw_off[i] = (uint32_t)(row * D * 2 + ((ld_chunk ^ ksw) * 16));
+    vw_off[i] = (uint32_t)(row * D * 2 + ((ld_chunk ^ dswz<D>(row)) * 16));
+  }
+  // K fragment reads (A of S^T): key 16 kb + l16 of the step, d = 32 st + 8 g.
+  uint32_t kr_off[KS];
+  {
+    const int ksw = D == 128 ? (l16 & 15) : ((l16 >> 1) & 7);  // rows 16 kb + l16
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      kr_off[st] = (uint32_t)(l16 * D * 2 + (((4 * st + g) ^ ksw) * 16));
   }
   // Transposed V reads: in 16-lane group g, lane p points at row 32u + 4g + p/4 (+16
   // for the second half of the slots) and columns 16*db + 4*(p%4); the group receives
@@ -203,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 
   Pos cur = locate(gs), nxt = cur;
 
-  u32x4 kA[4][KS], kB[4][KS];  // two VGPR sets of K fragments
+  u32x4 kreg[NI], vreg[NI];  // one step of K and V rows on their way to LDS
   bf16x8 qf[KS];
   f32x4 acc[DB];
   float m_run = kNegInf, l_run = 0.f, l_lse = 0.f;
@@ -228,11 +247,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)(valid - 1) * row_bytes + D * 2);
     return dmake_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nrec);
   };
-  // Issue the loads of step `it`: K into `kf`, V into LDS stage.  Every cache byte is
-  // read once, so the loads are marked non-temporal.
-  auto issue = [&](const Pos& it, u32x4 (*kf)[KS], auto stage_c)
-      __attribute__((always_inline)) {
-    constexpr int stage = decltype(stage_c)::value;
+  // Issue the loads of step `it` into kreg / vreg.  Every cache byte is read once, so the
+  // loads are marked non-temporal.
+  auto issue = [&](const Pos& it) __attribute__((always_inline)) {
     const int n0 = it.i * kStep;
     __amdgpu_buffer_rsrc_t rk, rv;
     uint32_t soff;  // byte offset of the step's first key row inside the descriptor
@@ -248,17 +265,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       soff = (uint32_t)n0 * row_bytes;
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int i = 0; i < NI; ++i) {
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rk, ld_off + (uint32_t)(RPI * i) * row_bytes, soff, kNT);
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rv, ld_off + (uint32_t)(RPI * i) * row_bytes, soff, kNT);
+    }
+  };
+  // The landed step into this wave's LDS slice.
+  auto stage = [&]() __attribute__((always_inline)) {
+    char* kb8 = reinterpret_cast<char*>(kst[wave]);
+    char* vb8 = reinterpret_cast<char*>(vst[wave]);
 #pragma unroll
-      for (int st = 0; st < KS; ++st)
-        kf[kb][st] = __builtin_amdgcn_raw_buffer_load_b128(
-            rk, k_lane + 64u * st, soff + (uint32_t)(16 * kb) * row_bytes, kNT);
-    uint16_t* dst = stage == 1 ? vst1[wave] : vst0[wave];
-#pragma unroll
-    for (int i = 0; i < VI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (dlds_void_t*)(dst + i * 512), 16, v_lane[i & 1],
-          soff + (uint32_t)(i & ~1) * (64 / CH) * row_bytes, 0, kNT);
+    for (int i = 0; i < NI; ++i) {
+      *reinterpret_cast<u32x4*>(kb8 + kw_off[i]) = kreg[i];
+      *reinterpret_cast<u32x4*>(vb8 + vw_off[i]) = vreg[i];
+    }
   };
 
   auto item_begin = [&](const Pos& it) __attribute__((always_inline)) {
@@ -301,18 +323,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   };
 
   // One 64-key step: scores, online softmax, P V.
-  auto compute = [&](const Pos& it, u32x4 (*kf)[KS], auto stage_c)
-      __attribute__((always_inline)) {
-    constexpr int stage = decltype(stage_c)::value;
+  auto compute = [&](const Pos& it) __attribute__((always_inline)) {
     const int n0 = it.i * kStep;
+    const char* kb8 = reinterpret_cast<const char*>(kst[wave]);
     f32x4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       s[kb] = f32x4{};
 #pragma unroll
-      for (int st = 0; st < KS; ++st)
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kb][st]),
-                                                        qf[st], s[kb], 0, 0, 0);
+      for (int st = 0; st < KS; ++st) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb8 + kr_off[st] + kb * 16 * D * 2);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], s[kb], 0, 0, 0);
+      }
     }
     float mx = kNegInf;
     const int lim = it.L - 1 - (n0 + 4 * g);  // last valid key, relative to this lane's keys
@@ -356,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     }
     l_run = l_run * alpha + rs;
     const __attribute__((address_space(3))) char* vb =
-        (const __attribute__((address_space(3))) char*)(stage == 1 ? vst1[wave] : vst0[wave]);
+        (const __attribute__((address_space(3))) char*)(vst[wave]);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -394,35 +416,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     return true;
   };
 
-  // ---- software pipeline, unrolled by two for the two K register sets / LDS stages
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
+  // ---- pipeline: while step s is computed from LDS, the rows of step s+1 are in flight
+  // into kreg / vreg
   item_begin(cur);
-  issue(cur, kA, S0{});
-  auto half = [&](u32x4 (*kc)[KS], u32x4 (*kn)[KS], auto stage_c, auto other_c)
-      __attribute__((always_inline)) -> bool {
+  issue(cur);
+  while (true) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this step's rows (and queries) landed
+    stage();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): written; kreg / vreg free again
     const bool more = advance(cur, nxt);
-    if (more) {
-      issue(nxt, kn, other_c);
-      // wait for this step's loads: everything but the just-issued 4*KS + VI
-      static_assert(4 * KS + VI == 32 || 4 * KS + VI == 16, "vmcnt encoding");
-      if constexpr (4 * KS + VI == 32) __builtin_amdgcn_s_waitcnt(0x8f70);  // vmcnt(32)
-      else __builtin_amdgcn_s_waitcnt(0x4f70);                             // vmcnt(16)
-      compute(cur, kc, stage_c);
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-      compute(cur, kc, stage_c);
-    }
+    if (more) issue(nxt);
+    compute(cur);
     if (!more || nxt.S != cur.S) {
       item_end(cur);
       if (more) item_begin(nxt);
     }
+    if (!more) break;
     cur = nxt;
-    return more;
-  };
-  while (true) {
-    if (!half(kA, kB, S0{}, S1{})) break;
-    if (!half(kB, kA, S1{}, S0{})) break;
   }
 }
 
