@@ -12,20 +12,23 @@
 // Three kernels, in stream order, none of them with atomics (results are bitwise
 // reproducible):
 //   bwd_prep_kernel   D_i = sum_c dO_ic O_ic and lse2_i = LSE_i * log2(e), per (b, h, i).
-//   bwd_dkdv_kernel   one workgroup per 128 keys of one (batch, K/V head): K and V of
-//                     those keys stay in registers while the Q and dO tiles of every
-//                     query head of the GQA group stream through LDS; dK and dV
-//                     accumulate in registers and are written once.
+//   bwd_dkdv_kernel   one workgroup per 256 keys of one (batch, K/V head), 8 waves of
+//                     32 keys, two waves per SIMD: K of those keys sits in LDS and -V in
+//                     registers while the Q and dO tiles of every query head of the GQA
+//                     group stream through LDS; dK and dV accumulate in registers and
+//                     are written once.
 //   bwd_dq_kernel     one workgroup per 128 query rows of one (batch, query head): Q and
 //                     dO rows stay in registers while K and V tiles stream through LDS;
 //                     dQ accumulates in registers.
 // S and dP are therefore formed twice (once per output side), which trades 40% more
 // MFMA work for having no cross-workgroup reduction at all.
 //
-// MFMA layouts (v_mfma_f32_32x32x16_bf16, D = A B): the A operand of lane l is row l%32,
-// k = 8(l/32) .. +7; B is column l%32, the same k; D holds column l%32, rows
-// 8(r/4) + 4(l/32) + r%4 in register r.  Tiles in LDS are read both as rows (16-byte
-// reads) and transposed (ds_read_b64_tr_b16), so one XOR swizzle serves both.
+// MFMA layouts of the dQ kernel (v_mfma_f32_32x32x16_bf16, D = A B): the A operand of
+// lane l is row l%32, k = 8(l/32) .. +7; B is column l%32, the same k; D holds column
+// l%32, rows 8(r/4) + 4(l/32) + r%4 in register r.  The dK/dV kernel uses
+// v_mfma_f32_16x16x32_bf16: A lane l is row l%16, k = 8(l/16) .. +7; B column l%16, the
+// same k; D column l%16, rows 4(l/16) + r.  Tiles in LDS are read both as rows (16-byte
+// reads) and transposed (ds_read_b64_tr_b16), so one XOR swizzle per kernel serves both.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -38,7 +41,6 @@ constexpr int kTile = 64;  // rows per LDS tile (keys for dQ, query rows for dK/
 
 typedef __attribute__((address_space(3))) void blds_void_t;
 typedef __bf16 bbf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) bbf16x4 blds_bf16x4_t;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void* base, uint32_t bytes) {
@@ -164,20 +166,86 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------
-// dK, dV for 128 keys (32 per wave) of one (batch, K/V head).
+// dK, dV for 256 keys of one (batch, K/V head): 8 waves of 32 keys (two groups of 16),
+// two waves per SIMD.  The workgroup's K block sits in LDS and is read as the B operand of
+// S = Q K^T; -V stays in registers as the B operand of D - dP.  The dK and dV accumulators
+// (32 keys x D each) take half of the wave's 256 registers, which is why a wave holds 32
+// keys and not 64, and why K lives in LDS rather than in registers.
+//
+// With v_mfma_f32_16x16x32_bf16 a lane's S / dP accumulators hold one key (the column)
+// and four query rows, which is exactly the k slice the B operand of the dV^T += dO^T P
+// and (-dK)^T += Q^T (-dS) products needs from that lane: P and -dS go from the score
+// registers to the next product without a lane exchange.  The A operands of those two
+// products (dO^T, Q^T) are read transposed from the same tiles, with rows gathered in the
+// order the score layout produces them (4g .. 4g+3 and 16+4g .. 16+4g+3 of a 32-row
+// block for lane group g).
+constexpr int kKeysDKV = 256;  // keys per dK/dV workgroup
+
+// Chunk swizzle of this kernel's tiles (Q, dO and the K block).  ds_read_b128 serves 16
+// lanes per pass, the lanes of quads {0,3,5,6} (or {1,2,4,7}) of a half-wave together,
+// and the transposed reads serve a half-wave per pass (LDS bank structure measured with
+// the SQ_LDS_BANK_CONFLICT counter on gfx950).  The row reads here put 16 rows at one
+// logical chunk per 16-lane group, the transposed reads 8 rows x 2 chunks per half-wave;
+// with this XOR both patterns hit 16 distinct bank groups per pass.  (The dQ kernel's
+// swizzle, made for the 32x32 operand shapes, leaves 2-way conflicts on both.)
+template <int D>
+__device__ __forceinline__ int dkv_swz(int row) {
+  return D == 128 ? ((row & 7) << 1) : (row & 6);
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t dkv_row_chunk(int row, int chunk) {
+  return (uint32_t)(row * D * 2 + ((chunk ^ dkv_swz<D>(row)) * 16));
+}
+
+template <int D>
+struct DkvShape {
+  static constexpr int CH = D / 8;                            // 16-byte chunks per row
+  static constexpr int PER_WAVE = kTile * CH / 64 / 8;        // Q / dO tile, per wave
+  static constexpr int K_PER_WAVE = kKeysDKV * CH / 64 / 8;   // K block, per wave
+};
+
+// One 64-row Q or dO tile into LDS, 8 waves: each instruction fills 1 KB in lane order.
+template <int D>
+__device__ __forceinline__ void dkv_tile_offsets(uint32_t* off, uint32_t row_bytes, int wave,
+                                                 int lane) {
+#pragma unroll
+  for (int i = 0; i < DkvShape<D>::PER_WAVE; ++i) {
+    const int lin = (wave * DkvShape<D>::PER_WAVE + i) * 64 + lane;
+    const int row = lin / DkvShape<D>::CH;
+    const int pos = lin % DkvShape<D>::CH;
+    off[i] = (uint32_t)row * row_bytes + (uint32_t)(pos ^ dkv_swz<D>(row)) * 16u;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dkv_tile_issue(__amdgpu_buffer_rsrc_t rs, const uint32_t* off,
+                                               uint32_t soff, uint16_t* tile, int wave) {
+#pragma unroll
+  for (int i = 0; i < DkvShape<D>::PER_WAVE; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (blds_void_t*)(tile + (wave * DkvShape<D>::PER_WAVE + i) * 512), 16, off[i], soff,
+        0, 0);
+}
+
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(1, 1))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512),
+                          amdgpu_waves_per_eu(2, 2))) void
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ Dws, const float* __restrict__ L2ws,
                 float* __restrict__ dK, float* __restrict__ dV, int B, int Hq, int Hkv, int Nq,
                 int Nk, float c, float scale, int n_kblocks) {
-  constexpr int PW = TileShape<D>::PER_WAVE;
+  constexpr int PW = DkvShape<D>::PER_WAVE;
+  constexpr int KPW = DkvShape<D>::K_PER_WAVE;
+  constexpr int CH = DkvShape<D>::CH;
+  constexpr int KS = D / 32;  // 32-wide d steps of the S and dP products
+  constexpr int DB = D / 16;  // 16-row d blocks of dK^T and dV^T
   __shared__ __attribute__((aligned(1024))) uint16_t qs0[kTile * D];
   __shared__ __attribute__((aligned(1024))) uint16_t qs1[kTile * D];
   __shared__ __attribute__((aligned(1024))) uint16_t os0[kTile * D];
   __shared__ __attribute__((aligned(1024))) uint16_t os1[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t kls[kKeysDKV * D];
   __shared__ __attribute__((aligned(16))) float ls[2][2][kTile];  // [stage][lse2, D][row]
   // stage buffers picked with a select (a runtime-indexed array of LDS pointers would
   // need a static initializer the target cannot express)
@@ -187,8 +255,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  const int p16 = lane & 15;  // key within a 16-key group (column of S, dP)
+  const int g = lane >> 4;    // lane group: rows 4g .. 4g+3 of every 16-row block
 
   const int G = Hq / Hkv;
   // one workgroup per bundle; key block 0 (seen by the most query rows) is the heaviest
@@ -197,50 +265,84 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int bk = w.group;
   const int kvh = bk % Hkv;
   const int b = bk / Hkv;
-  const int n0 = kblk * 128;
-  const int key = n0 + wave * 32 + l32;  // this lane's key (column of S, dP, P, dS)
-  const int diag = Nk - Nq;              // key j visible from row i iff j <= i + diag
+  const int n0 = kblk * kKeysDKV;
+  const int kw0 = n0 + wave * 32;  // first key of this wave; its keys are kw0 + 16 kg + p16
+  const int diag = Nk - Nq;        // key j visible from row i iff j <= i + diag
 
   const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
   const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
 
-  // K^T and -V^T fragments of this lane's key (B operands; zeros past Nk).  V enters
-  // negated (exact in bf16) so that the dP product, started from D instead of 0, yields
-  // D - dP directly: the softmax gradient needs no subtraction, and dK comes out negated.
-  bf16x8 kf[D / 16], vf[D / 16];
+  // the workgroup's K block straight into LDS (rows past Nk read as zeros)
   {
     const __amdgpu_buffer_rsrc_t rk =
         brsrc(K + ((size_t)b * Nk * Hkv + kvh) * D, (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int lin = (wave * KPW + i) * 64 + lane;
+      const int row = lin / CH;
+      const int pos = lin % CH;
+      const uint32_t off =
+          (uint32_t)(n0 + row) * kv_row_bytes + (uint32_t)(pos ^ dkv_swz<D>(row)) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (blds_void_t*)(kls + (wave * KPW + i) * 512),
+                                               16, off, 0, 0, 0);
+    }
+  }
+  // -V^T B operands of this lane's two keys, d = 32 s + 8 g .. +7 (zeros past Nk).  V
+  // enters negated (exact in bf16) so that the dP product, started from D instead of 0,
+  // yields D - dP directly: the softmax gradient needs no subtraction, and dK comes out
+  // negated.
+  bf16x8 vf[2][KS];
+  {
     const __amdgpu_buffer_rsrc_t rv =
         brsrc(V + ((size_t)b * Nk * Hkv + kvh) * D, (uint32_t)(Nk - 1) * kv_row_bytes + D * 2);
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      const uint32_t off = (uint32_t)key * kv_row_bytes + (uint32_t)(16 * st + 8 * hi) * 2;
-      kf[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vf[st] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0) ^ 0x80008000u);
-    }
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint32_t off =
+            (uint32_t)(kw0 + 16 * kg + p16) * kv_row_bytes + (uint32_t)(32 * s + 8 * g) * 2;
+        vf[kg][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0) ^ 0x80008000u);
+      }
   }
 
-  // query tiles that can see any of the 128 keys: rows >= n0 - diag under the causal
-  // mask; tiles from row n0 + 127 - diag on see all of them and need no mask
+  // query tiles that can see any of the 256 keys: rows >= n0 - diag under the causal
+  // mask; tiles from row n0 + 255 - diag on see all of them and need no mask
   const int n_mt = (Nq + kTile - 1) / kTile;
   const int m_first = CAUSAL ? min(max(0, n0 - diag) / kTile, n_mt) : 0;
-  const int m_full = CAUSAL ? min((max(0, n0 + 127 - diag) + kTile - 1) / kTile, n_mt) : 0;
+  const int m_full =
+      CAUSAL ? min((max(0, n0 + kKeysDKV - 1 - diag) + kTile - 1) / kTile, n_mt) : 0;
   const int n_it = (n_mt - m_first) * G;
   const int n_open = (n_mt - m_full) * G;  // the first n_open iterations are unmasked
 
-  f32x16 dkt[D / 32], dvt[D / 32];
+  f32x4 dkt[2][DB], dvt[2][DB];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    dkt[i] = f32x16{};
-    dvt[i] = f32x16{};
-  }
+  for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      dkt[kg][i] = f32x4{};
+      dvt[kg][i] = f32x4{};
+    }
 
-  uint32_t toff[D / 32][2];
-  tr_offsets<D>(toff, lane);
+  // row reads (A operands of S and dP, B operands from the K block): row 16x + p16,
+  // chunk 4s + g; the swizzle depends on the row's low four bits only, so the 16-row
+  // block and the key group enter as immediate offsets
+  uint32_t roff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) roff[s] = dkv_row_chunk<D>(p16, 4 * s + g);
+  // transposed reads: lane p16 of group g points at row 4g + p16/4 and columns
+  // 16 db + 4 (p16 % 4) .. +3, and the group receives X[row0 + i][16 db + p16].  The
+  // offset for d block db is block 0's with 32 db XORed in: the swizzle permutes chunks,
+  // and block db's two chunks differ from block 0's only in bits 1.. of the chunk index.
+  uint32_t toff0;
+  {
+    const int row = 4 * g + (p16 >> 2);
+    const int dcol = 4 * (p16 & 3);
+    toff0 = (uint32_t)(row * D * 2 + (((dcol >> 3) ^ dkv_swz<D>(row)) * 16) + (dcol & 7) * 2);
+  }
   uint32_t tl[PW];
-  tile_offsets<D>(tl, q_row_bytes, wave, lane);
+  dkv_tile_offsets<D>(tl, q_row_bytes, wave, lane);
+  const char* kt = reinterpret_cast<const char*>(kls) + wave * 32 * D * 2;
 
   // iteration t -> query tile n_mt-1 - t/G, query head t%G of the group: the workgroups of
   // one K/V head that run together all start at the last tile and step through the same
@@ -254,8 +356,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         brsrc(Q + ((size_t)b * Nq * Hq + hq) * D, (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
     const __amdgpu_buffer_rsrc_t ro =
         brsrc(dO + ((size_t)b * Nq * Hq + hq) * D, (uint32_t)(Nq - 1) * q_row_bytes + D * 2);
-    tile_issue<D>(rq, tl, (uint32_t)m * q_row_bytes, qs(stage), wave);
-    tile_issue<D>(ro, tl, (uint32_t)m * q_row_bytes, os(stage), wave);
+    dkv_tile_issue<D>(rq, tl, (uint32_t)m * q_row_bytes, qs(stage), wave);
+    dkv_tile_issue<D>(ro, tl, (uint32_t)m * q_row_bytes, os(stage), wave);
     if (wave < 2) {
       // rows past Nq read as 0: lse2 = 0 and D = 0 there, and Q, dO rows are 0 too, so
       // those rows add nothing to dK or dV
@@ -266,138 +368,113 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  // one iteration on LDS stage ST (a compile-time constant, so every LDS address is a
-  // loop-invariant register plus an immediate), with or without the causal mask
-  auto step = [&](auto ST, auto MASK, int t) __attribute__((always_inline)) {
-    constexpr int st = decltype(ST)::value;
+  // one iteration, with or without the causal mask.  The stage is a runtime value: with
+  // the two stages unrolled into one loop body the compiler renames the 32 accumulator
+  // registers between the copies and runs out of registers.
+  auto step = [&](auto MASK, int t) __attribute__((always_inline)) {
+    const int st = t & 1;
     constexpr bool masked = decltype(MASK)::value;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's part of tile t has landed
     __syncthreads();                      // ... everyone's; stage st^1 is free again
     if (t + 1 < n_it) issue(t + 1, st ^ 1);
     const char* qt = reinterpret_cast<const char*>(qs(st));
     const char* ot = reinterpret_cast<const char*>(os(st));
+    const __attribute__((address_space(3))) char* ob =
+        (const __attribute__((address_space(3))) char*)(os(st));
+    const __attribute__((address_space(3))) char* qb =
+        (const __attribute__((address_space(3))) char*)(qs(st));
+    // tile row r sees key kw0 + 16 kg + p16 iff r >= kmin + 16 kg
+    const int kmin = kw0 + p16 - diag - tile_of(t) * kTile;
 
-    // per 32-row half: S = Q K^T and D - dP = D + dO (-V)^T, then the softmax gradient,
-    // then the dV / dK products; written so half 1's products overlap half 0's VALU work
-    f32x16 s[2], dp[2];
-    u32x4 pw[4], dw[4];
-    const int kmin = key - diag - tile_of(t) * kTile;  // tile row r sees the key iff r >= kmin
-    auto sdp = [&](int rh) __attribute__((always_inline)) {
-      s[rh] = f32x16{};
-      {
-        // D of the rows this lane's accumulator registers hold: 8 q4 + 4 hi + 0..3
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&ls[st][1][32 * rh + 4 * hi]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&ls[st][1][32 * rh + 8 + 4 * hi]);
-        const f32x4 d2 = *reinterpret_cast<const f32x4*>(&ls[st][1][32 * rh + 16 + 4 * hi]);
-        const f32x4 d3 = *reinterpret_cast<const f32x4*>(&ls[st][1][32 * rh + 24 + 4 * hi]);
-        const f32x8 d01 = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7);
-        const f32x8 d23 = __builtin_shufflevector(d2, d3, 0, 1, 2, 3, 4, 5, 6, 7);
-        dp[rh] = __builtin_shufflevector(d01, d23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12,
-                                         13, 14, 15);
-      }
-      bf16x8 aq[D / 16], ao[D / 16];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int row = 32 * rh + l32;
-        aq[kk] = *reinterpret_cast<const bf16x8*>(qt + row_chunk<D>(row, 2 * kk + hi));
-        ao[kk] = *reinterpret_cast<const bf16x8*>(ot + row_chunk<D>(row, 2 * kk + hi));
-      }
-      // all 16 operand reads go out before the first product: left to itself the compiler
-      // issues each read just ahead of its MFMA and the one wave per SIMD then waits out
-      // the LDS latency before every product
-      __builtin_amdgcn_sched_barrier(0);
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      u32x4 pw[2], dw[2];  // P and -dS of the 32-row block kb2 as B operands, per key group
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], kf[kk], s[rh], 0, 0, 0);
-        dp[rh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[kk], vf[kk], dp[rh], 0, 0, 0);
-      }
-    };
-    // P = 2^(S c - lse2) and -dS = P (D - dP), packed to bf16 as B operands
-    auto grad = [&](int rh) __attribute__((always_inline)) {
+      for (int h = 0; h < 2; ++h) {
+        const int rb = 2 * kb2 + h;
+        // S = Q K^T and D - dP = D + dO (-V)^T for rows 16 rb .. +15
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(&ls[st][1][16 * rb + 4 * g]);
+        f32x4 s[2] = {f32x4{}, f32x4{}};
+        f32x4 dp[2] = {dd, dd};
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int r0 = 32 * rh + 8 * q4 + 4 * hi;
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&ls[st][0][r0]);
-        float pv[4], dv4[4];
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qt + roff[ks] + rb * 16 * D * 2);
+          const bf16x8 ao = *reinterpret_cast<const bf16x8*>(ot + roff[ks] + rb * 16 * D * 2);
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-          float p = fast_exp2(fmaf(s[rh][4 * q4 + t4], c, -l2[t4]));
-          if (masked) p = (r0 + t4 >= kmin) ? p : 0.f;
-          pv[t4] = p;
-          dv4[t4] = p * dp[rh][4 * q4 + t4];
+          for (int kg = 0; kg < 2; ++kg) {
+            const bf16x8 kk = *reinterpret_cast<const bf16x8*>(kt + roff[ks] + kg * 16 * D * 2);
+            s[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kk, s[kg], 0, 0, 0);
+            dp[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vf[kg][ks], dp[kg], 0, 0, 0);
+          }
         }
-        const int u = 2 * rh + (q4 >> 1);
-        const int w = 2 * (q4 & 1);
-        pw[u][w] = pack_bf16x2(pv[0], pv[1]);
-        pw[u][w + 1] = pack_bf16x2(pv[2], pv[3]);
-        dw[u][w] = pack_bf16x2(dv4[0], dv4[1]);
-        dw[u][w + 1] = pack_bf16x2(dv4[2], dv4[3]);
-      }
-    };
-    auto accum = [&](int rh) __attribute__((always_inline)) {
-      bf16x8 ao[2][D / 32], aq[2][D / 32];
+        // P = 2^(S c - lse2) and -dS = P (D - dP), packed to bf16
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&ls[st][0][16 * rb + 4 * g]);
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu)
+        for (int kg = 0; kg < 2; ++kg) {
+          float pv[4], dv4[4];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          ao[uu][db] = tr_operand<D>(os(st), toff, db, 2 * rh + uu);
-          aq[uu][db] = tr_operand<D>(qs(st), toff, db, 2 * rh + uu);
-        }
-      __builtin_amdgcn_sched_barrier(0);  // likewise: the 32 transposed reads first
-#pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
-        const int u = 2 * rh + uu;
-        const bf16x8 pp = __builtin_bit_cast(bf16x8, pw[u]);
-        const bf16x8 dsp = __builtin_bit_cast(bf16x8, dw[u]);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[uu][db], pp, dvt[db], 0, 0, 0);
-          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[uu][db], dsp, dkt[db], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            float pp = fast_exp2(fmaf(s[kg][i], c, -l2[i]));
+            if (masked) pp = (16 * rb + 4 * g + i >= kmin + 16 * kg) ? pp : 0.f;
+            pv[i] = pp;
+            dv4[i] = pp * dp[kg][i];
+          }
+          pw[kg][2 * h] = pack_bf16x2(pv[0], pv[1]);
+          pw[kg][2 * h + 1] = pack_bf16x2(pv[2], pv[3]);
+          dw[kg][2 * h] = pack_bf16x2(dv4[0], dv4[1]);
+          dw[kg][2 * h + 1] = pack_bf16x2(dv4[2], dv4[3]);
         }
       }
-    };
-    sdp(0);
-    sdp(1);
-    grad(0);
-    accum(0);
-    grad(1);
-    accum(1);
+      // dV^T += dO^T P and (-dK)^T += Q^T (-dS) over the 32 rows of block kb2
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint32_t tdb = toff0 ^ (uint32_t)(32 * db);
+        const bbf16x4 o0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (blds_bf16x4_t*)(ob + tdb + (32 * kb2) * D * 2));
+        const bbf16x4 o1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (blds_bf16x4_t*)(ob + tdb + (32 * kb2 + 16) * D * 2));
+        const bbf16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (blds_bf16x4_t*)(qb + tdb + (32 * kb2) * D * 2));
+        const bbf16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (blds_bf16x4_t*)(qb + tdb + (32 * kb2 + 16) * D * 2));
+        const bf16x8 ao = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+        const bf16x8 aq = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg) {
+          dvt[kg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              ao, __builtin_bit_cast(bf16x8, pw[kg]), dvt[kg][db], 0, 0, 0);
+          dkt[kg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              aq, __builtin_bit_cast(bf16x8, dw[kg]), dkt[kg][db], 0, 0, 0);
+        }
+        // issue each d block's four reads just ahead of its four products: left free, the
+        // compiler hoists all 32 reads and spills
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
   using Open = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, CAUSAL>;
-  // pairs of iterations, stage 0 then stage 1; the unmasked run is cut to an even length
-  // (a tile that needs no mask may still take the masked path)
   if (n_it > 0) issue(0, 0);
   int t = 0;
-  for (; t + 1 < (n_open & ~1); t += 2) {
-    step(S0{}, Open{}, t);
-    step(S1{}, Open{}, t + 1);
-  }
-  for (; t + 1 < n_it; t += 2) {
-    step(S0{}, Masked{}, t);
-    step(S1{}, Masked{}, t + 1);
-  }
-  if (t < n_it) step(S0{}, Masked{}, t);
+  for (; t < n_open; ++t) step(Open{}, t);
+  for (; t < n_it; ++t) step(Masked{}, t);
 
   // dK = scale * (Q^T dS)^T (the accumulator holds -Q^T dS), dV = (dO^T P)^T; lane = key,
-  // registers hold 4 consecutive d
-  if (key < Nk) {
-    float* krow = dK + (((size_t)b * Nk + key) * Hkv + kvh) * D;
-    float* vrow = dV + (((size_t)b * Nk + key) * Hkv + kvh) * D;
+  // registers hold d = 16 db + 4g .. +3
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int kg = 0; kg < 2; ++kg) {
+    const int key = kw0 + 16 * kg + p16;
+    if (key < Nk) {
+      float* krow = dK + (((size_t)b * Nk + key) * Hkv + kvh) * D;
+      float* vrow = dV + (((size_t)b * Nk + key) * Hkv + kvh) * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * hi;
-        *reinterpret_cast<f32x4*>(krow + col) =
-            f32x4{dkt[db][4 * g] * -scale, dkt[db][4 * g + 1] * -scale,
-                  dkt[db][4 * g + 2] * -scale, dkt[db][4 * g + 3] * -scale};
-        *reinterpret_cast<f32x4*>(vrow + col) =
-            f32x4{dvt[db][4 * g], dvt[db][4 * g + 1], dvt[db][4 * g + 2], dvt[db][4 * g + 3]};
+      for (int db = 0; db < DB; ++db) {
+        const int col = 16 * db + 4 * g;
+        *reinterpret_cast<f32x4*>(krow + col) = dkt[kg][db] * -scale;
+        *reinterpret_cast<f32x4*>(vrow + col) = dvt[kg][db];
       }
+    }
   }
 }
 
@@ -593,9 +670,9 @@ hipError_t launch(const BackwardArgs& a, hipStream_t s) {
                      0, s, a.o, static_cast<const uint16_t*>(a.dout), a.lse, a.dsum, a.lse2,
                      a.B, a.Hq, a.Nq);
   const float c = a.scale * kLog2e;
-  const int n_kblocks = (a.Nk + 127) / 128;
+  const int n_kblocks = (a.Nk + kKeysDKV - 1) / kKeysDKV;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_kblocks * a.B * a.Hkv)),
-                     dim3(256), 0, s, static_cast<const uint16_t*>(a.q),
+                     dim3(512), 0, s, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.dsum, a.lse2, a.dk, a.dv, a.B, a.Hq,
                      a.Hkv, a.Nq, a.Nk, c, a.scale, n_kblocks);
