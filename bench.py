@@ -365,7 +365,7 @@ def bench_backward(fa, W, pcfg, dev, K):
             "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_call_ms": round(avg, 4),
             "median_call_ms": round(sorted(ms)[K // 2], 4), "flop_per_call": flops,
             "executed_tflops": round(tf * 7 / 5, 2), "workload": pcfg.workload,
-            "kernels": "prep (D, lse2) + dK/dV per 128 keys + dQ per 128 rows (one call)"}
+            "kernels": "prep (D, lse2) + dK/dV per 256 keys + dQ per 128 rows (one call)"}
 
 
 def bench_prefill_leg(fa, W, name, dev, launches, min_seconds=0.3):

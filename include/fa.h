@@ -191,7 +191,7 @@ size_t fa_backward_workspace_bytes(int B, int Hq, int Nq);
  * (computed as sum_c dO_ic O_ic), dS = P (dP - D), dQ = scale dS K, dK = scale dS^T Q.
  * P = exp(scale Q K^T - LSE) uses the forward's LSE directly.  GQA: the dK and dV of a
  * K/V head add up its Hq / Hkv query heads.  Deterministic (no atomics): one kernel
- * forms dK and dV per block of 128 keys, another dQ per block of 128 query rows, each
+ * forms dK and dV per block of 256 keys, another dQ per block of 128 query rows, each
  * recomputing the S and dP blocks it needs.
  *
  *   q, k, v     as in fa_forward (bf16)                          (read)
