@@ -556,21 +556,6 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   if (threadIdx.x == 0) LSE[row] = (nc > 0) ? Mtr + fast_log2(St) * kLn2 : kNegInf;
 }
 
-// Compute units of the current device, queried once per device and kept (the value
-// never changes while the process runs; racing first calls store the same number).
-int device_cus() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  int v = cached[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-    v = 256;
-  cached[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
-
 template <int D, bool PAGED>
 hipError_t launch(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
@@ -592,6 +577,21 @@ hipError_t launch(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Compute units of the current device, queried once per device and kept (the value
+// never changes while the process runs; racing first calls store the same number).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t s) {
   if (a.block_table != nullptr)

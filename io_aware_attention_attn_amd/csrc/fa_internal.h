@@ -86,6 +86,9 @@ struct Fp8Args {
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_prefill_fp8(const Fp8Args& a, hipStream_t s);
+// Compute units of the current device (queried once per device; 256 if the query fails).
+int device_cus();
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_splitkv(const DecodeArgs& a, hipStream_t s);

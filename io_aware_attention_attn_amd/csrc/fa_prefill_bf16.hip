@@ -49,6 +49,10 @@
 //     so every XCD gets equal work (xcd_work).
 //   * Causal: key blocks wholly in the future of the workgroup's rows are never
 //     visited; only blocks crossing the diagonal or the ragged end are masked.
+//   * Small grids (at most two workgroups per CU, fixed-length batches): the workgroup
+//     has two key groups of WAVES waves on the same query rows, taking alternate key
+//     blocks; group 1 hands its state to group 0 through LDS at the end, and group 0
+//     merges the two states by the two-block rule before the epilogue.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -136,28 +140,41 @@ struct Varlen {
   int q_stride, kv_stride;
 };
 
-template <int D, int WAVES, bool CAUSAL, bool VARLEN>
-__global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64, WAVES * 64),
+// KSPLIT: two groups of WAVES waves share the workgroup's query rows and split its key
+// blocks between them (group g takes blocks g, g+2, g+4, ...), each with its own LDS
+// stages; at the end group 1 hands its running state (reference, sums, accumulator)
+// through LDS and group 0 merges it with its own by the two-block rule ([FA-notes] §4)
+// before the epilogue.  For grids too small to fill the GPU: the key loop of a workgroup
+// halves and each SIMD gets a second wave.
+template <int D, int WAVES, bool CAUSAL, bool VARLEN, bool KSPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(WAVES * 64 * (KSPLIT ? 2 : 1),
+                                                      WAVES * 64 * (KSPLIT ? 2 : 1)),
                           amdgpu_waves_per_eu(2, 2))) void
 prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     const uint16_t* __restrict__ V, float* __restrict__ O,
                     float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk, float c,
                     int n_mblocks, Varlen vl) {
   static_assert(D == 64 || D == 128, "head dim");
+  static_assert(!(KSPLIT && VARLEN), "key groups are for fixed-length batches");
   constexpr int BM = 32 * WAVES;
+  constexpr int NG = KSPLIT ? 2 : 1;  // key groups
   // One array per stage: the compiler's wait insertion can then tell an LDS-DMA
   // write into one stage from reads of the other, and does not stall the reads of
-  // the current block on the prefetch of the next one.
-  __shared__ __attribute__((aligned(1024))) uint16_t ks0[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t ks1[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs0[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs1[kBN * D];
+  // the current block on the prefetch of the next one.  With key groups each stage
+  // holds one block per group.
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[NG * kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks1[NG * kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[NG * kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs1[NG * kBN * D];
   uint16_t* const ks[2] = {ks0, ks1};
   uint16_t* const vs[2] = {vs0, vs1};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = KSPLIT ? wave_all / WAVES : 0;  // key group
+  const int wave = KSPLIT ? wave_all % WAVES : wave_all;  // row wave within the group
+  const uint32_t goff = (uint32_t)grp * kBN * D;  // this group's block inside a stage (elements)
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -226,9 +243,12 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   const int diag = Nk - Nq;  // key j visible from row i iff j <= i + diag
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, min(m0 + BM, Nq) - 1 + diag + 1);
-  const int n = (kend + kBN - 1) / kBN;
+  const int n_all = (kend + kBN - 1) / kBN;
+  // this group's blocks: absolute block index j * NG + grp for j = 0 .. n - 1
+  const int n = KSPLIT ? (n_all - grp + 1) / 2 : n_all;
+  auto absj = [&](int j) __attribute__((always_inline)) { return j * NG + grp; };
   if constexpr (VARLEN) {
-    if (n <= 0) {
+    if (n_all <= 0) {
       // no key visible from any row of the block (no keys, or causal with more queries
       // than keys): the rows' softmax is empty -> O = 0, LSE = -inf
       const int r = m0 + tid / 2;  // two threads per row, D/2 columns each
@@ -262,7 +282,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     const int sk = Swz<D>::k(l32);  // (kb*32 + l32) has the same swizzle for both kb
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
-      koff[st] = (uint32_t)(l32 * D * 2 + (((2 * st + hi) ^ sk) * 16));
+      koff[st] = goff * 2 + (uint32_t)(l32 * D * 2 + (((2 * st + hi) ^ sk) * 16));
   }
   // V (A of O^T) through transposed reads: in each 16-lane group, lane p points at
   // row key0 + p/4 and columns d0 + 4*(p%4) .. +3; the group then receives
@@ -276,7 +296,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int dcol = 32 * db + 16 * (g & 1) + 4 * (p & 3);
-      voff[db] = (uint32_t)(rowl * D * 2 + (((dcol >> 3) ^ sv) * 16) + (dcol & 7) * 2);
+      voff[db] = goff * 2 + (uint32_t)(rowl * D * 2 + (((dcol >> 3) ^ sv) * 16) + (dcol & 7) * 2);
     }
   }
 
@@ -411,15 +431,18 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   };
 
   // ---- prologue: K(0), V(0), K(1) in flight; S(0), its mask and max
-  issue_block<D, WAVES>(rk, kvo, 0, ks[0], wave);
-  issue_block<D, WAVES>(rv, vvo, 0, vs[0], wave);
-  if (n > 1) issue_block<D, WAVES>(rk, kvo, kBN * kv_row_bytes, ks[1], wave);
   f32x16 s_a[2], s_b[2];
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  __syncthreads();
-  qk(ks[0], s_a);
-  if (need_mask(0)) mask(s_a, 0);
-  m_ref = fmaxf(row_max(s_a, 0), row_max(s_a, 1));  // first reference (acc, sums still 0)
+  if (!KSPLIT || n > 0) {
+    issue_block<D, WAVES>(rk, kvo, (uint32_t)absj(0) * kBN * kv_row_bytes, ks[0] + goff, wave);
+    issue_block<D, WAVES>(rv, vvo, (uint32_t)absj(0) * kBN * kv_row_bytes, vs[0] + goff, wave);
+    if (n > 1)
+      issue_block<D, WAVES>(rk, kvo, (uint32_t)absj(1) * kBN * kv_row_bytes, ks[1] + goff, wave);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    qk(ks[0], s_a);
+    if (need_mask(absj(0))) mask(s_a, absj(0));
+    m_ref = fmaxf(row_max(s_a, 0), row_max(s_a, 1));  // first reference (acc, sums still 0)
+  }
 
   // ---- software pipeline.  Iteration j (scores of block j already masked):
   //   phase 1: MFMA S(j+1) = K(j+1) Q^T          | VALU softmax of keys 0..31 of block j
@@ -435,8 +458,10 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's K(j+1), V(j) have landed
     __syncthreads();                      // ... and everyone's; stage sc of K is free
     if (j + 2 < n)
-      issue_block<D, WAVES>(rk, kvo, (uint32_t)(j + 2) * kBN * kv_row_bytes, ks[sc], wave);
-    issue_block<D, WAVES>(rv, vvo, (uint32_t)(j + 1) * kBN * kv_row_bytes, vs[1 - sc], wave);
+      issue_block<D, WAVES>(rk, kvo, (uint32_t)absj(j + 2) * kBN * kv_row_bytes, ks[sc] + goff,
+                            wave);
+    issue_block<D, WAVES>(rv, vvo, (uint32_t)absj(j + 1) * kBN * kv_row_bytes, vs[1 - sc] + goff,
+                          wave);
     bf16x8 pf[kBN / 16];
     qk(ks[1 - sc], s_nxt);
     float ex, rs;
@@ -445,7 +470,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     // it past the mask branch, next to its only consumer, and nothing would overlap.
     asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pf[0])), "v"(__builtin_bit_cast(u32x4, pf[1])),
                  "v"(ex), "v"(rs));
-    if (need_mask(j + 1)) mask(s_nxt, j + 1);
+    if (need_mask(absj(j + 1))) mask(s_nxt, absj(j + 1));
     commit_half(s_cur, pf, 0, ex, rs);
     pv(vs[sc], pf, 0);
     exp_pack(s_cur, pf, 1, ex, rs);
@@ -475,8 +500,46 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
   if (j + 1 < n) {
     step_next(S0{}, j, s_a, s_b);
     step_last(S1{}, s_b);
-  } else {
+  } else if (!KSPLIT || n > 0) {
     step_last(S0{}, s_a);
+  }
+
+  if constexpr (KSPLIT) {
+    // every wave passes the same number of barriers: group 0 has n0 + 1 of them (prologue
+    // and one per block), group 1 one fewer when the block count is odd, none if it got
+    // no block
+    const int n0 = (n_all + 1) / 2;
+    const int mine = n > 0 ? n + 1 : 0;
+    for (int i = mine; i < n0 + 1; ++i) __syncthreads();
+    __syncthreads();  // every wave is past its last read of the stage arrays
+    // group 1 hands over its state: accumulator in its own part of the stage arrays
+    // (one array per row wave), reference and sums in mst
+    __shared__ float mst[WAVES][3][64];
+    uint16_t* const arr = wave == 0 ? ks0 : wave == 1 ? ks1 : wave == 2 ? vs0 : vs1;
+    float* dump = reinterpret_cast<float*>(arr + kBN * D);  // group 1's block of that array
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dump[(db * 16 + r) * 64 + lane] = acc[db][r];
+      mst[wave][0][lane] = m_ref;
+      mst[wave][1][lane] = l_run;
+      mst[wave][2][lane] = l_lse;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = mst[wave][0][lane];
+    const float mn = fmaxf(m_ref, m1);
+    const float a0 = (m_ref == kNegInf) ? 0.f : fast_exp2(m_ref - mn);
+    const float a1 = (m1 == kNegInf) ? 0.f : fast_exp2(m1 - mn);
+    l_run = l_run * a0 + mst[wave][1][lane] * a1;
+    l_lse = l_lse * a0 + mst[wave][2][lane] * a1;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        acc[db][r] = fmaf(acc[db][r], a0, dump[(db * 16 + r) * 64 + lane] * a1);
+    m_ref = mn;
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
@@ -506,10 +569,22 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s) {
   const int n_mblocks = (a.Nq + BM - 1) / BM;
   const long long blocks = (long long)n_mblocks * a.B * a.Hq;
   const Varlen vl{a.cu_q, a.cu_k, a.total_q, a.total_k, a.q_stride, a.kv_stride};
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, WAVES, CAUSAL, VARLEN>), dim3((unsigned)blocks),
-                     dim3(WAVES * 64), 0, s, static_cast<const uint16_t*>(a.q),
-                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.o,
-                     a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_mblocks, vl);
+  // a grid of at most two workgroups per CU (the two-waves-per-SIMD occupancy of the
+  // plain kernel) leaves the GPU waiting on the key loops of its heaviest blocks: two key
+  // groups halve them and give every SIMD a second wave
+  if (!VARLEN && blocks <= 2LL * device_cus() && a.Nk > 2 * kBN) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, WAVES, CAUSAL, false, true>),
+                       dim3((unsigned)blocks), dim3(2 * WAVES * 64), 0, s,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq,
+                       a.Nk, a.scale * kLog2e, n_mblocks, vl);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, WAVES, CAUSAL, VARLEN, false>),
+                     dim3((unsigned)blocks), dim3(WAVES * 64), 0, s,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+                     a.scale * kLog2e, n_mblocks, vl);
   return hipGetLastError();
 }
 

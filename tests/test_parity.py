@@ -177,6 +177,9 @@ def test_c5_decode_full():
 # edge shapes, full oracle
 # ---------------------------------------------------------------------------
 
+# These grids hold at most two workgroups per CU, so every shape with Nk > 128 runs the
+# kernel's two-key-group form (alternate key blocks per group, states merged at the end);
+# the Nk <= 128 shapes and the larger c2-c4 workloads run the plain form.
 EDGE = [  # B, Nq, Nk, Hq, Hkv, d, causal, gain
     (1, 1, 1, 1, 1, 64, True, 1.0),
     (1, 1, 1000, 2, 1, 128, False, 1.0),

@@ -124,8 +124,10 @@ def test_varlen_packed_qkv_view():
 @pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
 def test_varlen_equals_fixed_length_bitwise(d, causal):
     """Equal lengths: the packed launch runs the same blocks with the same arithmetic as
-    fa_forward, so O and LSE agree bit for bit (only the layout differs)."""
-    B, N, Hq, Hkv = 3, 700, 8, 2
+    fa_forward, so O and LSE agree bit for bit (only the layout differs).  The grid (576
+    workgroups) is above two per CU, where fa_forward would split the key loop of each
+    workgroup over two key groups."""
+    B, N, Hq, Hkv = 3, 2048, 12, 4
     dev = _dev()
     q, k, v = W.prefill_inputs(B, Hq, Hkv, N, N, d, seed=5)
     o_f, lse_f = fa.fa_forward(q.to(dev), k.to(dev), v.to(dev), causal=causal)
