@@ -573,7 +573,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, causal>",
                      "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": (profiled_traffic("prefill_bf16_kernel<128, 4, true, false>")
+                     "traffic": (profiled_traffic("prefill_bf16_kernel<128, 4, true, false, false>")
                                  if pcfg.d == 128 and pcfg.causal else None),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                      "avg_launch_ms": round(avg_pre, 4),
