@@ -397,3 +397,20 @@ def test_binding_allocates_on_the_launch_stream(monkeypatch):
         assert seen_alloc, f"call {i} allocated nothing"
         assert all(isinstance(t, FakeStream) for t in seen_alloc), i
         assert seen_launch == [FakeStream.cuda_stream], i
+
+
+def test_bench_traffic_lookups_name_profiled_kernels():
+    """The kernel instantiations bench.py reads HBM traffic for (roofline.traffic, the decode
+    traffic) are keys of profiles/hbm_traffic.json, i.e. the names rocprofv3 reports for the
+    current kernels; a renamed instantiation would otherwise turn the figure into null."""
+    import ast
+    import json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    tree = ast.parse(open(os.path.join(root, "bench.py")).read())
+    names = [n.args[0].value for n in ast.walk(tree)
+             if isinstance(n, ast.Call) and getattr(n.func, "id", None) == "profiled_traffic"
+             and n.args and isinstance(n.args[0], ast.Constant)]
+    assert names, "bench.py reads no profiled traffic"
+    profiled = json.load(open(os.path.join(root, "profiles", "hbm_traffic.json")))
+    for name in names:
+        assert name in profiled, name
