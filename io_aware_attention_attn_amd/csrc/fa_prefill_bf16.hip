@@ -49,7 +49,7 @@
 //     so every XCD gets equal work (xcd_work).
 //   * Causal: key blocks wholly in the future of the workgroup's rows are never
 //     visited; only blocks crossing the diagonal or the ragged end are masked.
-//   * Small grids (at most two workgroups per CU, fixed-length batches): the workgroup
+//   * Small grids (at most two workgroups per CU): the workgroup
 //     has two key groups of WAVES waves on the same query rows, taking alternate key
 //     blocks; group 1 hands its state to group 0 through LDS at the end, and group 0
 //     merges the two states by the two-block rule before the epilogue.
@@ -155,7 +155,6 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
                     float* __restrict__ LSE, int B, int Hq, int Hkv, int Nq, int Nk, float c,
                     int n_mblocks, Varlen vl) {
   static_assert(D == 64 || D == 128, "head dim");
-  static_assert(!(KSPLIT && VARLEN), "key groups are for fixed-length batches");
   constexpr int BM = 32 * WAVES;
   constexpr int NG = KSPLIT ? 2 : 1;  // key groups
   // One array per stage: the compiler's wait insertion can then tell an LDS-DMA
@@ -572,8 +571,8 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s) {
   // a grid of at most two workgroups per CU (the two-waves-per-SIMD occupancy of the
   // plain kernel) leaves the GPU waiting on the key loops of its heaviest blocks: two key
   // groups halve them and give every SIMD a second wave
-  if (!VARLEN && blocks <= 2LL * device_cus() && a.Nk > 2 * kBN) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, WAVES, CAUSAL, false, true>),
+  if (blocks <= 2LL * device_cus() && a.Nk > 2 * kBN) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, WAVES, CAUSAL, VARLEN, true>),
                        dim3((unsigned)blocks), dim3(2 * WAVES * 64), 0, s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq,
