@@ -303,8 +303,12 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
   float m_ref = kNegInf;  // exponent reference (running max, possibly lagging), base 2
-  float l_run = 0.f;      // this lane's share of the row sum of the bf16-rounded weights
-  float l_lse = 0.f;      // ... and of the unrounded weights (for the LSE)
+  float neg_m = 0.f;      // -m_ref, or 0 while the reference is still -inf
+  // This lane's share of the row sums, each in two independent chains: the unrounded
+  // weights (for the LSE) and the bf16-rounded ones (O's normaliser).
+  float ls_a = 0.f, ls_b = 0.f;
+  float lr_a = 0.f, lr_b = 0.f;
+  float lim = kSumCap;    // the unrounded sum after the last half block, plus kSumCap
 
   uint32_t kvo[BlockShape<D, WAVES>::PER_WAVE], vvo[BlockShape<D, WAVES>::PER_WAVE];
   block_offsets<D, WAVES, false>(kvo, kv_row_bytes, wave, lane);
@@ -352,24 +356,25 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     const float m_new = fmaxf(m_ref, m_blk);
     // a row that has seen no visible key yet keeps alpha = 1
     const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_ref - m_new);
-    l_run *= alpha;
-    l_lse *= alpha;
+    ls_a *= alpha;
+    ls_b *= alpha;
+    lr_a *= alpha;
+    lr_b *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
     m_ref = m_new;
+    neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
   };
 
   // P = exp2(S*c - m_ref) for keys 32h .. 32h + 31 of the block (score registers s[h],
-  // P fragments pf[2h], pf[2h + 1]) and this lane's two partial row sums over them: `ex`
-  // of the fp32 weights (for the LSE) and `rs` of the bf16-rounded ones (v_dot2 with
-  // (1, 1)); O's normaliser adds up exactly the rounded weights, so O = acc / l is a true
-  // weighted mean of V whatever the reference.
-  auto exp_pack = [&](f32x16* s, bf16x8* pf, int h, float& ex, float& rs)
+  // P fragments pf[2h], pf[2h + 1]), with this lane's weights added to the running sums
+  // passed in: ea/eb the fp32 weights (for the LSE), ra/rb the bf16-rounded ones (v_dot2
+  // with (1, 1)); O's normaliser adds up exactly the rounded weights, so O = acc / l is a
+  // true weighted mean of V whatever the reference.
+  auto exp_pack = [&](f32x16* s, bf16x8* pf, int h, float& ea, float& eb, float& ra, float& rb)
       __attribute__((always_inline)) {
-    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
-    float ex0 = 0.f, ex1 = 0.f, rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu) {
       const int u = 2 * h + uu;
@@ -380,31 +385,39 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
       for (int t = 0; t < 4; ++t) {
         const float p0 = fast_exp2(fmaf(s[kb][base + 2 * t], c, neg_m));
         const float p1 = fast_exp2(fmaf(s[kb][base + 2 * t + 1], c, neg_m));
-        ex0 += p0;
-        ex1 += p1;
+        ea += p0;
+        eb += p1;
         w[t] = pack_bf16x2(p0, p1);
-        if (t & 1) rs1 = sum_bf16x2(w[t], rs1);
-        else rs0 = sum_bf16x2(w[t], rs0);
+        if (t & 1) rb = sum_bf16x2(w[t], rb);
+        else ra = sum_bf16x2(w[t], ra);
       }
       pf[u] = __builtin_bit_cast(bf16x8, w);
     }
-    ex = ex0 + ex1;
-    rs = rs0 + rs1;
   };
 
-  // Fold one half block's weights into the running sums.  A lane whose half-block sum
-  // exceeds the cap (a score well above the reference, or a reference still at -inf)
-  // sends the wave through the rare path: reference moved to the half block's row max
-  // (the part of O already accumulated is rescaled with the sums), half block
-  // recomputed.  NaN sums take that path too and then propagate.
-  auto commit_half = [&](f32x16* s, bf16x8* pf, int h, float ex, float rs)
+  // Fold one half block's weights into the running sums (exp_pack has already added them
+  // to the copies ea..rb).  A lane whose unrounded sum grew by more than kSumCap over the
+  // half block (a score well above the reference, or a reference still at -inf) sends the
+  // wave through the rare path: reference moved to the half block's row max (the part of
+  // O already accumulated is rescaled with the sums), half block recomputed.  NaN sums
+  // take that path too and then propagate.
+  auto commit_half = [&](f32x16* s, bf16x8* pf, int h, float ea, float eb, float ra, float rb)
       __attribute__((always_inline)) {
-    if (__builtin_amdgcn_ballot_w64(!(ex <= kSumCap)) != 0) {
+    float tot = ea + eb;
+    if (__builtin_amdgcn_ballot_w64(!(tot <= lim)) != 0) {
       rescale_to(row_max(s, h));
-      exp_pack(s, pf, h, ex, rs);
+      ea = ls_a;
+      eb = ls_b;
+      ra = lr_a;
+      rb = lr_b;
+      exp_pack(s, pf, h, ea, eb, ra, rb);
+      tot = ea + eb;
     }
-    l_lse += ex;
-    l_run += rs;
+    ls_a = ea;
+    ls_b = eb;
+    lr_a = ra;
+    lr_b = rb;
+    lim = tot + kSumCap;
   };
 
   // O^T += V^T P^T over keys 32h .. 32h + 31 of the block, V^T through transposed LDS
@@ -425,8 +438,11 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
       }
   };
 
+  // Block j needs the mask if it runs past the last key, or (causal) past the last key
+  // visible from this wave's first row.
+  const int wrow0 = m0 + wave * 32;
   auto need_mask = [&](int j) __attribute__((always_inline)) {
-    return (j * kBN + kBN > Nk) || (CAUSAL && (j * kBN + kBN - 1 > m0 + diag));
+    return (j * kBN + kBN > Nk) || (CAUSAL && (j * kBN + kBN - 1 > wrow0 + diag));
   };
 
   // ---- prologue: K(0), V(0), K(1) in flight; S(0), its mask and max
@@ -441,6 +457,7 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     qk(ks[0], s_a);
     if (need_mask(absj(0))) mask(s_a, absj(0));
     m_ref = fmaxf(row_max(s_a, 0), row_max(s_a, 1));  // first reference (acc, sums still 0)
+    neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
   }
 
   // ---- software pipeline.  Iteration j (scores of block j already masked):
@@ -463,17 +480,18 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
                           wave);
     bf16x8 pf[kBN / 16];
     qk(ks[1 - sc], s_nxt);
-    float ex, rs;
-    exp_pack(s_cur, pf, 0, ex, rs);
+    float ea = ls_a, eb = ls_b, ra = lr_a, rb = lr_b;
+    exp_pack(s_cur, pf, 0, ea, eb, ra, rb);
     // Keep the exp/pack work in this block: without a use here the compiler would sink
     // it past the mask branch, next to its only consumer, and nothing would overlap.
     asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pf[0])), "v"(__builtin_bit_cast(u32x4, pf[1])),
-                 "v"(ex), "v"(rs));
+                 "v"(ea), "v"(eb), "v"(ra), "v"(rb));
     if (need_mask(absj(j + 1))) mask(s_nxt, absj(j + 1));
-    commit_half(s_cur, pf, 0, ex, rs);
+    commit_half(s_cur, pf, 0, ea, eb, ra, rb);
     pv(vs[sc], pf, 0);
-    exp_pack(s_cur, pf, 1, ex, rs);
-    commit_half(s_cur, pf, 1, ex, rs);
+    ea = ls_a, eb = ls_b, ra = lr_a, rb = lr_b;
+    exp_pack(s_cur, pf, 1, ea, eb, ra, rb);
+    commit_half(s_cur, pf, 1, ea, eb, ra, rb);
     pv(vs[sc], pf, 1);
   };
   auto step_last = [&](auto stage_c, f32x16* s_cur) __attribute__((always_inline)) {
@@ -483,9 +501,9 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     bf16x8 pf[kBN / 16];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float ex, rs;
-      exp_pack(s_cur, pf, h, ex, rs);
-      commit_half(s_cur, pf, h, ex, rs);
+      float ea = ls_a, eb = ls_b, ra = lr_a, rb = lr_b;
+      exp_pack(s_cur, pf, h, ea, eb, ra, rb);
+      commit_half(s_cur, pf, h, ea, eb, ra, rb);
       pv(vs[sc], pf, h);
     }
   };
@@ -503,6 +521,8 @@ prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
     step_last(S0{}, s_a);
   }
 
+  float l_run = lr_a + lr_b;  // this lane's share of the row sum of the bf16-rounded weights
+  float l_lse = ls_a + ls_b;  // ... and of the unrounded weights (for the LSE)
   if constexpr (KSPLIT) {
     // every wave passes the same number of barriers: group 0 has n0 + 1 of them (prologue
     // and one per block), group 1 one fewer when the block count is odd, none if it got
