@@ -95,9 +95,11 @@ __device__ __forceinline__ void tile8_issue(__amdgpu_buffer_rsrc_t rs, const uin
         0);
 }
 
-// four fp32 -> four E4M3 codes in one dword (byte i = x_i), round to nearest even
-__device__ __forceinline__ int pack_e4m3x4(float x0, float x1, float x2, float x3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+// four fp32 -> four E4M3 codes in one dword (byte i = x_i), round to nearest even.  The
+// first conversion writes the low half only and keeps the high half of `old`, which the
+// second overwrites: passing the dword's previous (dead) contents saves a register clear.
+__device__ __forceinline__ int pack_e4m3x4(float x0, float x1, float x2, float x3, int old) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, old, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
 }
 
@@ -203,7 +205,10 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
   f32x16 lsum = {};         // row sums of the E4M3 weights (every register holds the sum)
   float m_ref = kNegInf;    // exponent reference, base 2
-  float l_lse = 0.f;        // this lane's share of the row sum of the fp32 weights
+  float neg_m = 0.f;        // -m_ref, or 0 while the reference is still -inf
+  // this lane's share of the row sum of the fp32 weights, in two independent chains
+  float ls_a = 0.f, ls_b = 0.f;
+  float lim = kSumCap8;     // that sum after the last block, plus kSumCap8
   const i32x8 ones = {kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3,
                       kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3};
 
@@ -249,7 +254,8 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
   auto rescale_to = [&](float m_blk) __attribute__((always_inline)) {
     const float m_new = fmaxf(m_ref, m_blk);
     const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_ref - m_new);
-    l_lse *= alpha;
+    ls_a *= alpha;
+    ls_b *= alpha;
 #pragma unroll
     for (int r = 0; r < 16; ++r) lsum[r] *= alpha;
 #pragma unroll
@@ -257,14 +263,14 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
     m_ref = m_new;
+    neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
   };
 
   // P^T = exp2(S^T c - m_ref) packed as the B operand of the second product: dword 2a
   // holds keys 32hi + 8a + 0..3 (registers 4a.. of s[0]), dword 2a+1 keys 32hi + 8a + 4..7
-  // (registers 4a.. of s[1]); `ex` is this lane's fp32 sum.
-  auto exp_pack = [&](const f32x16* s, i32x8& pf, float& ex) __attribute__((always_inline)) {
-    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
-    float e0 = 0.f, e1 = 0.f;
+  // (registers 4a.. of s[1]); the fp32 weights are added to the running sums ea, eb.
+  auto exp_pack = [&](const f32x16* s, i32x8& pf, float& ea, float& eb)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -272,11 +278,10 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
         float p[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) p[t] = fast_exp2(fmaf(s[kb][4 * a + t], c, neg_m));
-        e0 += p[0] + p[1];
-        e1 += p[2] + p[3];
-        pf[2 * a + kb] = pack_e4m3x4(p[0], p[1], p[2], p[3]);
+        ea += p[0] + p[1];
+        eb += p[2] + p[3];
+        pf[2 * a + kb] = pack_e4m3x4(p[0], p[1], p[2], p[3], pf[2 * a + kb]);
       }
-    ex = e0 + e1;
   };
 
   // O^T += V^T P^T and the E4M3 row sums (ones^T P^T)
@@ -295,20 +300,31 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     lsum = mfma8(ones, pf, lsum);
   };
 
+  // block j needs the mask if it runs past the last key, or (causal) past the last key
+  // visible from this wave's first row
+  const int wrow0 = m0 + wave * 32;
   auto need_mask = [&](int j) __attribute__((always_inline)) {
-    return (j * kBN8 + kBN8 > Nk) || (CAUSAL && (j * kBN8 + kBN8 - 1 > m0 + diag));
+    return (j * kBN8 + kBN8 > Nk) || (CAUSAL && (j * kBN8 + kBN8 - 1 > wrow0 + diag));
   };
 
-  // a block's softmax with the rare reference move (see the bf16 prefill)
-  auto softmax = [&](f32x16* s, i32x8& pf, float ex) __attribute__((always_inline)) {
-    if (__builtin_amdgcn_ballot_w64(!(ex <= kSumCap8)) != 0) {
+  // a block's softmax with the rare reference move (see the bf16 prefill): taken when a
+  // lane's fp32 sum grew by more than kSumCap8 over the block
+  auto softmax = [&](f32x16* s, i32x8& pf, float ea, float eb) __attribute__((always_inline)) {
+    float tot = ea + eb;
+    if (__builtin_amdgcn_ballot_w64(!(tot <= lim)) != 0) {
       rescale_to(row_max(s));
-      exp_pack(s, pf, ex);
+      ea = ls_a;
+      eb = ls_b;
+      exp_pack(s, pf, ea, eb);
+      tot = ea + eb;
     }
-    l_lse += ex;
+    ls_a = ea;
+    ls_b = eb;
+    lim = tot + kSumCap8;
   };
 
   f32x16 s_a[2], s_b[2];
+  i32x8 pf = {};  // P^T of the block in flight (each block's packing overwrites it)
   if (n > 0) {
     tile8_issue<D>(rk, kvo, 0, ks[0], wave);
     tile8_issue<D>(rv, vvo, 0, vs[0], wave);
@@ -318,6 +334,7 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     qk(ks[0], s_a);
     if (need_mask(0)) mask(s_a, 0);
     m_ref = row_max(s_a);
+    neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
   }
 
   // iteration j: MFMA S(j+1) | VALU softmax of block j; then MFMA O += V(j)^T P(j)^T
@@ -330,22 +347,20 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
       tile8_issue<D>(rk, kvo, (uint32_t)(j + 2) * kBN8 * kv_row_bytes, ks[sc], wave);
     tile8_issue<D>(rv, vvo, (uint32_t)(j + 1) * kBN8 * kv_row_bytes, vs[1 - sc], wave);
     qk(ks[1 - sc], s_nxt);
-    i32x8 pf;
-    float ex;
-    exp_pack(s_cur, pf, ex);
-    asm volatile("" ::"v"(pf), "v"(ex));
+    float ea = ls_a, eb = ls_b;
+    exp_pack(s_cur, pf, ea, eb);
+    asm volatile("" ::"v"(pf), "v"(ea), "v"(eb));
     if (need_mask(j + 1)) mask(s_nxt, j + 1);
-    softmax(s_cur, pf, ex);
+    softmax(s_cur, pf, ea, eb);
     pv(vs[sc], pf);
   };
   auto step_last = [&](auto stage_c, f32x16* s_cur) __attribute__((always_inline)) {
     constexpr int sc = decltype(stage_c)::value;
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    i32x8 pf;
-    float ex;
-    exp_pack(s_cur, pf, ex);
-    softmax(s_cur, pf, ex);
+    float ea = ls_a, eb = ls_b;
+    exp_pack(s_cur, pf, ea, eb);
+    softmax(s_cur, pf, ea, eb);
     pv(vs[sc], pf);
   };
   using S0 = std::integral_constant<int, 0>;
@@ -363,7 +378,7 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
   }
 
   // O = v_descale * acc / (sum of E4M3 weights), LSE = ln2 (m_ref + log2(sum of fp32 weights))
-  const float l_ex = xor32_sum(l_lse);
+  const float l_ex = xor32_sum(ls_a + ls_b);
   const float inv = v_descale / lsum[0];
   if (qrow < Nq) {
     float* Orow = O + (((size_t)b * Nq + qrow) * Hq + hq) * D;
