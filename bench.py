@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement (reported beside the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the board power / clock sampling under the prefill")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calib", action="store_true",
@@ -409,6 +411,62 @@ def bench_prefill_leg(fa, W, name, dev, launches, min_seconds=0.3):
             "kernel": f"prefill_bf16_kernel<{cfg.d}, causal>"}
 
 
+def power_leg(run, sync, seconds=4.0):
+    """Board power and engine clocks while `run` (one prefill launch) repeats back to back.
+
+    Samples `amd-smi metric -g 0 -p -c` (socket power, per-XCD GFX clocks) every ~0.3 s
+    from a child process; the first two samples (clock ramp) are dropped.  None when
+    amd-smi is not available."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(smi):
+        return None
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([smi, "metric", "-g", "0", "-p", "-c"], capture_output=True,
+                                   text=True, timeout=20)
+            except (OSError, subprocess.SubprocessError):
+                return
+            pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
+            clks = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz",
+                                                 r.stdout)]
+            if pw and clks:
+                samples.append((float(pw.group(1)), clks))
+            stop.wait(0.3)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        run()
+        n += 1
+        if n % 4 == 0:
+            sync()
+    sync()
+    stop.set()
+    th.join(timeout=30)
+    use = samples[2:] if len(samples) > 4 else samples
+    if not use:
+        return None
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    watts = [w for w, _ in use]
+    clk_mean = [sum(c) / len(c) for _, c in use]
+    return {"socket_power_w_median": med(watts), "socket_power_w_max": max(watts),
+            "gfx_clock_mhz_median": round(med(clk_mean), 1),
+            "gfx_clock_mhz_range": [min(min(c) for _, c in use), max(max(c) for _, c in use)],
+            "board_power_limit_w": 1400, "samples": len(use), "launches": n,
+            "source": "amd-smi metric -g 0 -p -c every ~0.3 s while the prefill launch repeats "
+                      "back to back (board limit: the published MI355X total board power)"}
+
+
 def decode_piece_steps(lengths, dcfg, cus):
     """The decode's real split: all (batch, K/V head, head group) segments laid end to end
     in 64-key steps, T steps in all, cut into equal runs of R = max(ceil(T / W), chunk / 64)
@@ -581,6 +639,12 @@ def main():
                      "flop_per_launch": flops},
         "wall_s_timed_region": round(wall, 3),
     }
+    if not args.no_power:
+        print("[bench] power and clocks under the prefill", file=sys.stderr, flush=True)
+        pw = power_leg(prefill, torch.cuda.synchronize)
+        if pw is not None:
+            pw["pj_per_flop"] = round(pw["socket_power_w_median"] / (tflops * 1e12) * 1e12, 3)
+        result["roofline"]["power"] = pw
     if dec:
         dbytes = W.decode_bytes(dec["lengths"].tolist(), dcfg.Hq, dcfg.Hkv, dcfg.d)
         dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
