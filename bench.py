@@ -411,13 +411,23 @@ def bench_prefill_leg(fa, W, name, dev, launches, min_seconds=0.3):
             "kernel": f"prefill_bf16_kernel<{cfg.d}, causal>"}
 
 
+def parse_smi_metric(text):
+    """(socket power in W, [GFX clock of each XCD in MHz]) from `amd-smi metric -p -c` text,
+    or None when either is missing."""
+    import re
+    pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
+    clks = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text)]
+    if not pw or not clks:
+        return None
+    return float(pw.group(1)), clks
+
+
 def power_leg(run, sync, seconds=4.0):
     """Board power and engine clocks while `run` (one prefill launch) repeats back to back.
 
     Samples `amd-smi metric -g 0 -p -c` (socket power, per-XCD GFX clocks) every ~0.3 s
     from a child process; the first two samples (clock ramp) are dropped.  None when
     amd-smi is not available."""
-    import re
     import shutil
     import subprocess
     import threading
@@ -434,11 +444,9 @@ def power_leg(run, sync, seconds=4.0):
                                    text=True, timeout=20)
             except (OSError, subprocess.SubprocessError):
                 return
-            pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
-            clks = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz",
-                                                 r.stdout)]
-            if pw and clks:
-                samples.append((float(pw.group(1)), clks))
+            got = parse_smi_metric(r.stdout)
+            if got is not None:
+                samples.append(got)
             stop.wait(0.3)
 
     th = threading.Thread(target=sampler, daemon=True)

@@ -414,3 +414,34 @@ def test_bench_traffic_lookups_name_profiled_kernels():
     profiled = json.load(open(os.path.join(root, "profiles", "hbm_traffic.json")))
     for name in names:
         assert name in profiled, name
+
+
+def test_bench_parses_amd_smi_power_and_clocks():
+    """bench.py's power leg reads the socket power and the per-XCD GFX clocks from the text
+    `amd-smi metric -p -c` prints (layout of ROCm 7.2's amd-smi: a POWER block, then one
+    GFX_k block per XCD whose first line is its current clock); other clock blocks and the
+    MIN/MAX lines are not taken."""
+    import bench
+    text = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1349 W
+        GFX_VOLTAGE: N/A
+        THROTTLE_STATUS: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1751 MHz
+            MIN_CLK: 157 MHz
+            MAX_CLK: 2400 MHz
+            CLK_LOCKED: DISABLED
+        GFX_1:
+            CLK: 1655 MHz
+            MIN_CLK: 157 MHz
+            MAX_CLK: 2400 MHz
+        MEM_0:
+            CLK: 2000 MHz
+            MIN_CLK: 900 MHz
+        VCLK_0:
+            CLK: 59 MHz
+"""
+    assert bench.parse_smi_metric(text) == (1349.0, [1751.0, 1655.0])
+    assert bench.parse_smi_metric("GPU: 0\n    POWER:\n        SOCKET_POWER: N/A\n") is None
