@@ -64,7 +64,8 @@ def parse():
                     help="skip the backward-pass measurement (reported beside the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-power", action="store_true",
-                    help="skip the board power / clock sampling under the prefill")
+                    help="skip the board power / clock sampling under the prefill and the "
+                         "matrix-core ceiling leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calib", action="store_true",
@@ -422,18 +423,17 @@ def parse_smi_metric(text):
     return float(pw.group(1)), clks
 
 
-def power_leg(run, sync, seconds=4.0):
-    """Board power and engine clocks while `run` (one prefill launch) repeats back to back.
-
-    Samples `amd-smi metric -g 0 -p -c` (socket power, per-XCD GFX clocks) every ~0.3 s
-    from a child process; the first two samples (clock ramp) are dropped.  None when
-    amd-smi is not available."""
+def power_sampled(workload):
+    """Runs `workload()` while a child process samples `amd-smi metric -g 0 -p -c` (socket
+    power, per-XCD GFX clocks) every ~0.3 s; returns (workload's result, power summary).
+    The first two samples (clock ramp) are dropped; the summary is None when amd-smi is
+    not available."""
     import shutil
     import subprocess
     import threading
     smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
     if not os.path.exists(smi):
-        return None
+        return workload(), None
     samples = []
     stop = threading.Event()
 
@@ -451,28 +451,88 @@ def power_leg(run, sync, seconds=4.0):
 
     th = threading.Thread(target=sampler, daemon=True)
     th.start()
-    t0 = time.perf_counter()
-    n = 0
-    while time.perf_counter() - t0 < seconds:
-        run()
-        n += 1
-        if n % 4 == 0:
-            sync()
-    sync()
-    stop.set()
-    th.join(timeout=30)
+    try:
+        res = workload()
+    finally:
+        stop.set()
+        th.join(timeout=30)
     use = samples[2:] if len(samples) > 4 else samples
     if not use:
-        return None
+        return res, None
     med = lambda xs: sorted(xs)[len(xs) // 2]
     watts = [w for w, _ in use]
     clk_mean = [sum(c) / len(c) for _, c in use]
-    return {"socket_power_w_median": med(watts), "socket_power_w_max": max(watts),
-            "gfx_clock_mhz_median": round(med(clk_mean), 1),
-            "gfx_clock_mhz_range": [min(min(c) for _, c in use), max(max(c) for _, c in use)],
-            "board_power_limit_w": 1400, "samples": len(use), "launches": n,
-            "source": "amd-smi metric -g 0 -p -c every ~0.3 s while the prefill launch repeats "
-                      "back to back (board limit: the published MI355X total board power)"}
+    return res, {"socket_power_w_median": med(watts), "socket_power_w_max": max(watts),
+                 "gfx_clock_mhz_median": round(med(clk_mean), 1),
+                 "gfx_clock_mhz_range": [min(min(c) for _, c in use),
+                                         max(max(c) for _, c in use)],
+                 "board_power_limit_w": 1400, "samples": len(use),
+                 "source": "amd-smi metric -g 0 -p -c every ~0.3 s while the launch repeats "
+                           "back to back (board limit: the published MI355X total board power)"}
+
+
+def power_leg(run, sync, seconds=4.0):
+    """Board power and engine clocks while `run` (one prefill launch) repeats back to back
+    for `seconds`."""
+    def work():
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            run()
+            n += 1
+            if n % 4 == 0:
+                sync()
+        sync()
+        return n
+    n, pw = power_sampled(work)
+    if pw is not None:
+        pw["launches"] = n
+    return pw
+
+
+def mfma_ceiling_leg(fa, dev, seconds=4.0):
+    """The bf16 matrix cores' sustained rate under the same power limit (fa_probe_mfma_bf16:
+    independent 32x32x16 MFMAs on random bf16 register operands, no memory traffic, two
+    waves per SIMD like the prefill), timed with HIP events over back-to-back launches of
+    ~15 ms while power and clocks are sampled."""
+    import torch
+    print("[bench] matrix-core ceiling", file=sys.stderr, flush=True)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * cus
+    g = torch.Generator(device="cpu").manual_seed(7)
+    nb = fa.fa_probe_mfma_bf16_operand_bytes(blocks)
+    ops = torch.randn(nb // 2, generator=g).to(torch.bfloat16).to(dev)
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    iters = 100000
+    flop = fa.fa_probe_mfma_bf16(ops, out, blocks, iters)  # warm
+    torch.cuda.synchronize()
+
+    def work():
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        n = 0
+        e0.record()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(4):
+                fa.fa_probe_mfma_bf16(ops, out, blocks, iters)
+            n += 4
+            torch.cuda.synchronize()
+        e1.record()
+        e1.synchronize()
+        return n, e0.elapsed_time(e1)
+
+    (n, ms), pw = power_sampled(work)
+    assert torch.isfinite(out).all().item()
+    tflops = flop * n / (ms * 1e-3) / 1e12
+    return {"value": round(tflops, 1), "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+            "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "launches": n,
+            "avg_launch_ms": round(ms / n, 3), "power": pw,
+            "method": "fa_probe_mfma_bf16: per thread four independent v_mfma_f32_32x32x16_bf16 "
+                      "accumulators (VGPR form), every instruction on a different pair of random "
+                      "bf16 register operands, no memory traffic; "
+                      f"{blocks} workgroups of 256 threads (two waves per SIMD), {iters} "
+                      "iterations per launch"}
 
 
 def decode_piece_steps(lengths, dcfg, cus):
@@ -653,6 +713,9 @@ def main():
         if pw is not None:
             pw["pj_per_flop"] = round(pw["socket_power_w_median"] / (tflops * 1e12) * 1e12, 3)
         result["roofline"]["power"] = pw
+        ceil = mfma_ceiling_leg(fa, dev)
+        ceil["kernel_frac_of_ceiling"] = round(tflops / ceil["value"], 4)
+        result["roofline"]["mfma_ceiling"] = ceil
     if dec:
         dbytes = W.decode_bytes(dec["lengths"].tolist(), dcfg.Hq, dcfg.Hkv, dcfg.d)
         dec_ms = [e[2].elapsed_time(e[3]) for e in ev]

@@ -324,6 +324,23 @@ int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
  * string for a status code; unknown codes give "unknown fa_status". */
 const char* fa_status_str(int status);
 
+/*
+ * fa_probe_mfma_bf16 — measurement helper (not an operation of the method, no page
+ * passage): the sustained rate of the bf16 matrix cores, for comparing a kernel's rate
+ * with what the hardware delivers under the same power limit.  Launches `blocks`
+ * workgroups of 256 threads; every thread loads 8 x 16 bytes of `operands` (its four A
+ * and four B fragments, bf16) and runs `iters` iterations of four independent
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each) with no other memory traffic, then writes
+ * the sum of its accumulators to out[thread].  Work per launch: blocks * 4 * iters * 4 *
+ * 32768 FLOP.  operands: device buffer of at least fa_probe_mfma_bf16_operand_bytes(blocks)
+ * bytes (operand_bytes gives its size); out: device float[blocks * 256]; both 16-byte
+ * aligned and caller-owned.  Errors: FA_ERR_NULL, FA_ERR_SHAPE (blocks or iters not
+ * positive, blocks > 2^20, operands too small), FA_ERR_ALIGN, FA_ERR_HIP.
+ */
+size_t fa_probe_mfma_bf16_operand_bytes(int blocks);
+int fa_probe_mfma_bf16(const void* operands, size_t operand_bytes, float* out, int blocks,
+                       int iters, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

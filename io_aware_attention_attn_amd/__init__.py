@@ -25,6 +25,8 @@ Functions (same names as the C entry points):
   fa_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, scale=None, chunk=256,
                   o=None, lse=None, workspace=None, stream=None)
   fa_status_str(status)
+  fa_probe_mfma_bf16_operand_bytes(blocks), fa_probe_mfma_bf16(operands, out, blocks, iters,
+                     stream=None)   (measurement helper: the matrix cores' sustained rate)
 
 Allocation helper (not a C entry point; torch device memory only):
   kv_cache_empty(shape, device=None) -> (k_cache, v_cache)
@@ -91,12 +93,39 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_paged.restype = i
     L.fa_status_str.argtypes = [i]
     L.fa_status_str.restype = ctypes.c_char_p
+    L.fa_probe_mfma_bf16_operand_bytes.argtypes = [i]
+    L.fa_probe_mfma_bf16_operand_bytes.restype = sz
+    L.fa_probe_mfma_bf16.argtypes = [vp, sz, vp, i, i, vp]
+    L.fa_probe_mfma_bf16.restype = i
     _lib = L
     return L
 
 
 def fa_status_str(status: int) -> str:
     return lib().fa_status_str(int(status)).decode()
+
+
+def fa_probe_mfma_bf16_operand_bytes(blocks: int) -> int:
+    return int(lib().fa_probe_mfma_bf16_operand_bytes(int(blocks)))
+
+
+def fa_probe_mfma_bf16(operands, out, blocks: int, iters: int, stream=None):
+    """Measurement helper: `blocks` x 256 threads of independent bf16 32x32x16 MFMAs on
+    the operands in `operands` (a device tensor of at least
+    fa_probe_mfma_bf16_operand_bytes(blocks) bytes), each thread's accumulator sum to
+    `out` (float32, blocks * 256).  Returns the FLOP count of the launch."""
+    import torch
+    if not isinstance(operands, torch.Tensor) or not operands.is_cuda:
+        raise ValueError("operands must be a CUDA tensor")
+    _check_tensor(out, "out", torch.float32, 1)
+    if out.numel() < int(blocks) * 256:
+        raise ValueError("out is too small")
+    ts = _torch_stream(stream)
+    st = lib().fa_probe_mfma_bf16(_ptr(operands), operands.numel() * operands.element_size(),
+                                  _ptr(out), int(blocks), int(iters), int(ts.cuda_stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_probe_mfma_bf16")
+    return int(blocks) * 4 * int(iters) * 4 * 32768
 
 
 def _ptr(t) -> Optional[int]:

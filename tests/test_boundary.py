@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(L):
                           "fa_backward_workspace_bytes", "fa_backward",
                           "fa_decode_splitkv_workspace_bytes",
                           "fa_decode_splitkv", "fa_decode_splitkv_noalloc", "fa_decode_paged",
-                          "fa_status_str"}
+                          "fa_status_str", "fa_probe_mfma_bf16_operand_bytes",
+                          "fa_probe_mfma_bf16"}
     for n in names:
         assert hasattr(L, n), f"libfa.so does not export {n}"
 
@@ -445,3 +446,23 @@ def test_bench_parses_amd_smi_power_and_clocks():
 """
     assert bench.parse_smi_metric(text) == (1349.0, [1751.0, 1655.0])
     assert bench.parse_smi_metric("GPU: 0\n    POWER:\n        SOCKET_POWER: N/A\n") is None
+
+
+def test_probe_validation(L):
+    """The matrix-core probe checks its arguments before any HIP call."""
+    need = L.fa_probe_mfma_bf16_operand_bytes(4)
+    assert need == 4 * 256 * 8 * 16
+    assert L.fa_probe_mfma_bf16_operand_bytes(0) == 0
+    ok = dict(operands=P, nbytes=need, out=P, blocks=4, iters=10)
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.fa_probe_mfma_bf16(a["operands"], a["nbytes"], a["out"], a["blocks"],
+                                    a["iters"], None)
+    assert call(operands=None) == fa.FA_ERR_NULL
+    assert call(out=None) == fa.FA_ERR_NULL
+    assert call(blocks=0) == fa.FA_ERR_SHAPE
+    assert call(iters=0) == fa.FA_ERR_SHAPE
+    assert call(blocks=(1 << 20) + 1, nbytes=1 << 40) == fa.FA_ERR_SHAPE
+    assert call(nbytes=need - 1) == fa.FA_ERR_SHAPE
+    assert call(operands=MIS) == fa.FA_ERR_ALIGN
+    assert call(out=MIS) == fa.FA_ERR_ALIGN
