@@ -65,7 +65,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-power", action="store_true",
                     help="skip the board power / clock sampling under the prefill and the "
-                         "matrix-core ceiling leg")
+                         "ceiling legs (matrix cores, HBM streaming read)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calib", action="store_true",
@@ -535,6 +535,45 @@ def mfma_ceiling_leg(fa, dev, seconds=4.0):
                       "iterations per launch"}
 
 
+def stream_ceiling_leg(fa, dev, nbytes, launches=40):
+    """The HBM streaming-read rate on the same board (fa_probe_stream_read: every byte of a
+    buffer as large as the decode's K/V stream read once, 16 bytes per lane per load, the
+    decode's non-temporal cache policy, eight loads in flight per lane), over a few grid
+    sizes, each timed with HIP events over back-to-back launches; the best is reported."""
+    import torch
+    print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = min(int(nbytes) // 16 * 16, 1 << 31)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g,
+                        dtype=torch.int32).to(dev)
+    per = {}
+    for mult in (4, 8, 16):
+        blocks = mult * cus
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            fa.fa_probe_stream_read(buf, out, blocks)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            fa.fa_probe_stream_read(buf, out, blocks)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        per[f"{blocks}x256"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        del out
+    del buf
+    torch.cuda.empty_cache()
+    best = max(per.values())
+    return {"value": best, "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "frac_of_peak": round(best / PEAK_HBM_GBS, 4), "bytes": nbytes,
+            "launches_per_grid": launches, "by_grid": per,
+            "method": "fa_probe_stream_read: one pass over a buffer of the decode's byte count, "
+                      "16-byte non-temporal buffer loads, each wave instruction 1 KB "
+                      "contiguous, 32 KB chunks per workgroup, grid sizes as listed"}
+
+
 def decode_piece_steps(lengths, dcfg, cus):
     """The decode's real split: all (batch, K/V head, head group) segments laid end to end
     in 64-key steps, T steps in all, cut into equal runs of R = max(ceil(T / W), chunk / 64)
@@ -751,6 +790,10 @@ def main():
                                             "256 B past K's 1 KiB congruence class "
                                             "(kv_cache_empty)"}
         result["decode"]["separate_allocations"] = bench_decode_separate(fa, W, dcfg, dec, dev, K)
+        if not args.no_power:
+            sc = stream_ceiling_leg(fa, dev, dbytes)
+            sc["kernel_frac_of_ceiling"] = round(gbs / sc["value"], 4)
+            result["decode"]["stream_ceiling"] = sc
     if dec and not args.no_paged:
         result["decode_paged"] = bench_paged(fa, W, dcfg, dec, dev, K)
     if not args.no_varlen or not args.no_backward or not args.no_fp8 or not args.no_legs:

@@ -54,6 +54,7 @@
 #define FA_H
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -340,6 +341,22 @@ const char* fa_status_str(int status);
 size_t fa_probe_mfma_bf16_operand_bytes(int blocks);
 int fa_probe_mfma_bf16(const void* operands, size_t operand_bytes, float* out, int blocks,
                        int iters, hipStream_t stream);
+
+/*
+ * fa_probe_stream_read — measurement helper (not an operation of the method, no page
+ * passage): the HBM streaming-read rate, for comparing the decode's K/V stream with what
+ * plain reads of the same size reach on the same board.  Launches `blocks` workgroups of
+ * 256 threads that read every byte of `buf` once, 16 bytes per lane per load with the
+ * non-temporal cache policy of the decode's K/V loads, each workgroup taking 32 KB chunks
+ * `blocks` chunks apart; thread t of workgroup w writes the XOR of the 32-bit words it read
+ * to out[w * 256 + t] (the XOR over all of out equals the XOR of all words of buf).
+ * buf: device buffer of `bytes` bytes, 16-byte aligned, bytes a positive multiple of 16 and
+ * at most 2^31; out: device uint32[blocks * 256], 4-byte aligned; both caller-owned.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (blocks outside 1..65536, bytes out of range),
+ * FA_ERR_ALIGN, FA_ERR_HIP.
+ */
+int fa_probe_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,8 @@ Functions (same names as the C entry points):
   fa_status_str(status)
   fa_probe_mfma_bf16_operand_bytes(blocks), fa_probe_mfma_bf16(operands, out, blocks, iters,
                      stream=None)   (measurement helper: the matrix cores' sustained rate)
+  fa_probe_stream_read(buf, out, blocks, stream=None)
+                        (measurement helper: the HBM streaming-read rate)
 
 Allocation helper (not a C entry point; torch device memory only):
   kv_cache_empty(shape, device=None) -> (k_cache, v_cache)
@@ -97,6 +99,8 @@ def lib() -> ctypes.CDLL:
     L.fa_probe_mfma_bf16_operand_bytes.restype = sz
     L.fa_probe_mfma_bf16.argtypes = [vp, sz, vp, i, i, vp]
     L.fa_probe_mfma_bf16.restype = i
+    L.fa_probe_stream_read.argtypes = [vp, sz, vp, i, vp]
+    L.fa_probe_stream_read.restype = i
     _lib = L
     return L
 
@@ -126,6 +130,26 @@ def fa_probe_mfma_bf16(operands, out, blocks: int, iters: int, stream=None):
     if st != FA_OK:
         raise FAError(st, "fa_probe_mfma_bf16")
     return int(blocks) * 4 * int(iters) * 4 * 32768
+
+
+def fa_probe_stream_read(buf, out, blocks: int, stream=None):
+    """Measurement helper: `blocks` x 256 threads read every byte of `buf` (a contiguous
+    device tensor, 16-byte aligned, size a multiple of 16 bytes, at most 2^31) once and
+    write per-thread XORs of the 32-bit words read to `out` (int32, blocks * 256).
+    Returns the number of bytes read."""
+    import torch
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous CUDA tensor")
+    _check_tensor(out, "out", torch.int32, 1)
+    if out.numel() < int(blocks) * 256:
+        raise ValueError("out is too small")
+    nbytes = buf.numel() * buf.element_size()
+    ts = _torch_stream(stream)
+    st = lib().fa_probe_stream_read(_ptr(buf), nbytes, _ptr(out), int(blocks),
+                                    int(ts.cuda_stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_probe_stream_read")
+    return nbytes
 
 
 def _ptr(t) -> Optional[int]:

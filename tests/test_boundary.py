@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
                           "fa_decode_splitkv_workspace_bytes",
                           "fa_decode_splitkv", "fa_decode_splitkv_noalloc", "fa_decode_paged",
                           "fa_status_str", "fa_probe_mfma_bf16_operand_bytes",
-                          "fa_probe_mfma_bf16"}
+                          "fa_probe_mfma_bf16", "fa_probe_stream_read"}
     for n in names:
         assert hasattr(L, n), f"libfa.so does not export {n}"
 
@@ -466,3 +466,20 @@ def test_probe_validation(L):
     assert call(nbytes=need - 1) == fa.FA_ERR_SHAPE
     assert call(operands=MIS) == fa.FA_ERR_ALIGN
     assert call(out=MIS) == fa.FA_ERR_ALIGN
+
+
+def test_stream_probe_validation(L):
+    """The streaming-read probe checks its arguments before any HIP call."""
+    ok = dict(buf=P, nbytes=1 << 20, out=P, blocks=8)
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.fa_probe_stream_read(a["buf"], a["nbytes"], a["out"], a["blocks"], None)
+    assert call(buf=None) == fa.FA_ERR_NULL
+    assert call(out=None) == fa.FA_ERR_NULL
+    assert call(blocks=0) == fa.FA_ERR_SHAPE
+    assert call(blocks=(1 << 16) + 1) == fa.FA_ERR_SHAPE
+    assert call(nbytes=0) == fa.FA_ERR_SHAPE
+    assert call(nbytes=(1 << 20) + 8) == fa.FA_ERR_SHAPE
+    assert call(nbytes=(1 << 31) + 16) == fa.FA_ERR_SHAPE
+    assert call(buf=MIS) == fa.FA_ERR_ALIGN
+    assert call(out=P + 2) == fa.FA_ERR_ALIGN
