@@ -247,40 +247,52 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint32_t nrec = __builtin_amdgcn_readfirstlane((uint32_t)(valid - 1) * row_bytes + D * 2);
     return dmake_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nrec);
   };
-  // Issue the loads of step `it` into kreg / vreg.  Every cache byte is read once, so the
-  // loads are marked non-temporal.
-  auto issue = [&](const Pos& it) __attribute__((always_inline)) {
-    const int n0 = it.i * kStep;
+  // Where the rows of step `it` come from: the K and V descriptors and the byte offset of
+  // the step's first key row inside them.
+  struct Src {
     __amdgpu_buffer_rsrc_t rk, rv;
-    uint32_t soff;  // byte offset of the step's first key row inside the descriptor
+    uint32_t soff;
+  };
+  auto source = [&](const Pos& it) __attribute__((always_inline)) {
+    const int n0 = it.i * kStep;
+    Src src;
     if constexpr (PAGED) {
       const int p0 = __builtin_amdgcn_readfirstlane((n0 / pg.page_size) * pg.page_size);
       const int valid = min(pg.page_size, it.L - p0);
-      rk = page_rsrc(Kc, it.page, it.kvh, valid);
-      rv = page_rsrc(Vc, it.page, it.kvh, valid);
-      soff = (uint32_t)(n0 - p0) * row_bytes;
+      src.rk = page_rsrc(Kc, it.page, it.kvh, valid);
+      src.rv = page_rsrc(Vc, it.page, it.kvh, valid);
+      src.soff = (uint32_t)(n0 - p0) * row_bytes;
     } else {
-      rk = rsrc_of(Kc, it);
-      rv = rsrc_of(Vc, it);
-      soff = (uint32_t)n0 * row_bytes;
+      src.rk = rsrc_of(Kc, it);
+      src.rv = rsrc_of(Vc, it);
+      src.soff = (uint32_t)n0 * row_bytes;
     }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rk, ld_off + (uint32_t)(RPI * i) * row_bytes, soff, kNT);
-      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rv, ld_off + (uint32_t)(RPI * i) * row_bytes, soff, kNT);
-    }
+    return src;
   };
-  // The landed step into this wave's LDS slice.
-  auto stage = [&]() __attribute__((always_inline)) {
+  // Issue the K (or V) loads of a step into kreg (vreg).  Every cache byte is read once,
+  // so the loads are marked non-temporal.
+  auto issue_k = [&](const Src& src) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          src.rk, ld_off + (uint32_t)(RPI * i) * row_bytes, src.soff, kNT);
+  };
+  auto issue_v = [&](const Src& src) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          src.rv, ld_off + (uint32_t)(RPI * i) * row_bytes, src.soff, kNT);
+  };
+  // The landed K (or V) rows of a step into this wave's LDS slice.
+  auto stage_k = [&]() __attribute__((always_inline)) {
     char* kb8 = reinterpret_cast<char*>(kst[wave]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(kb8 + kw_off[i]) = kreg[i];
+  };
+  auto stage_v = [&]() __attribute__((always_inline)) {
     char* vb8 = reinterpret_cast<char*>(vst[wave]);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      *reinterpret_cast<u32x4*>(kb8 + kw_off[i]) = kreg[i];
-      *reinterpret_cast<u32x4*>(vb8 + vw_off[i]) = vreg[i];
-    }
+    for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(vb8 + vw_off[i]) = vreg[i];
   };
 
   auto item_begin = [&](const Pos& it) __attribute__((always_inline)) {
@@ -417,15 +429,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   };
 
   // ---- pipeline: while step s is computed from LDS, the rows of step s+1 are in flight
-  // into kreg / vreg
+  // into kreg / vreg.  K and V are staged one after the other, and each half's loads for
+  // step s+1 go out as soon as its registers are free, so the wave never drains its
+  // loads: the next K rows are on their way while this step's V rows are still landing
+  // (vector loads complete in issue order; the register uses below wait for exactly the
+  // loads they need).
   item_begin(cur);
-  issue(cur);
+  {
+    const Src src = source(cur);
+    issue_k(src);
+    issue_v(src);
+  }
   while (true) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this step's rows (and queries) landed
-    stage();
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): written; kreg / vreg free again
+    stage_k();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): written; kreg free again
     const bool more = advance(cur, nxt);
-    if (more) issue(nxt);
+    // After the last step the loads still go out, on an empty descriptor (no memory access,
+    // zeros back): with the same loads in flight on both paths the compiler's wait counts
+    // for the V rows below stay exact instead of falling back to the shorter path's.
+    Src src = {dmake_rsrc(Kc, 0u), dmake_rsrc(Vc, 0u), 0u};
+    if (more) src = source(nxt);
+    issue_k(src);
+    stage_v();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // vreg free again
+    issue_v(src);
     compute(cur);
     if (!more || nxt.S != cur.S) {
       item_end(cur);
