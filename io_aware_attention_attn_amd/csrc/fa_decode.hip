@@ -27,7 +27,9 @@
 //     whole head rows (4 rows x 256 bytes at d = 128): fetched 16 keys x 64 bytes per
 //     instruction, the layout the score product wants in registers, the same bytes
 //     stream about 9% slower.  A landed step is written to the wave's own LDS slice and
-//     the MFMA operands are read from there.
+//     the MFMA operands are read from there; K and V are written out one after the
+//     other and each half's next loads leave as soon as its registers are free, so a
+//     wave never drains its loads at a step boundary.
 //   * Scores S^T = K q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d read as rows
 //     from LDS, B = the group's query heads (up to 16, zero-padded).
 //     The matrix cores are far from busy; they are used because the group's query
