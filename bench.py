@@ -64,8 +64,9 @@ def parse():
                     help="skip the backward-pass measurement (reported beside the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-power", action="store_true",
-                    help="skip the board power / clock sampling under the prefill and the "
-                         "ceiling legs (matrix cores, HBM streaming read)")
+                    help="skip the board power / clock sampling (under the prefill and the "
+                         "other compute legs) and the ceiling legs (matrix cores, HBM "
+                         "streaming read)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calib", action="store_true",
@@ -290,9 +291,10 @@ def bench_varlen(fa, W, dev, K):
             "kernel": "prefill_bf16_kernel<128, causal, varlen>"}
 
 
-def bench_fp8(fa, W, pcfg, dev, K):
+def bench_fp8(fa, W, pcfg, dev, K, power=False):
     """fa_forward_fp8 on the prefill workload's shape (E4M3 codes of the same seeded draws,
-    per-tensor descales), timed on its own after the step; FLOP as the bf16 prefill."""
+    per-tensor descales), timed on its own after the step; FLOP as the bf16 prefill.  With
+    `power`, board power and clocks are then sampled while the launch repeats."""
     import torch
     print(f"[bench] fp8 forward on {pcfg.name}", file=sys.stderr, flush=True)
     q8, k8, v8, qd, kd, vd = W.fp8_inputs(pcfg.B, pcfg.Hq, pcfg.Hkv, pcfg.Nq, pcfg.Nk, pcfg.d,
@@ -319,19 +321,26 @@ def bench_fp8(fa, W, pcfg, dev, K):
     avg = sum(ms) / K
     flops = pcfg.flops()
     tf = flops / (avg * 1e-3) / 1e12
-    return {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_FP8_TFLOPS,
-            "frac": round(tf / PEAK_FP8_TFLOPS, 4), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "avg_launch_ms": round(avg, 4), "median_launch_ms": round(sorted(ms)[K // 2], 4),
-            "flop_per_launch": flops, "workload": pcfg.workload + " as E4M3 codes",
-            "kernel": "prefill_fp8_kernel<128, causal>"}
+    res = {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_FP8_TFLOPS,
+           "frac": round(tf / PEAK_FP8_TFLOPS, 4), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+           "avg_launch_ms": round(avg, 4), "median_launch_ms": round(sorted(ms)[K // 2], 4),
+           "flop_per_launch": flops, "workload": pcfg.workload + " as E4M3 codes",
+           "kernel": "prefill_fp8_kernel<128, causal>"}
+    if power:
+        pw = power_leg(call, torch.cuda.synchronize, seconds=3.0)
+        if pw is not None:
+            pw["pj_per_flop"] = round(pw["socket_power_w_median"] / (tf * 1e12) * 1e12, 3)
+        res["power"] = pw
+    return res
 
 
-def bench_backward(fa, W, pcfg, dev, K):
+def bench_backward(fa, W, pcfg, dev, K, power=False):
     """fa_backward on the prefill workload's shape (seeded Q, K, V, dO; O and LSE from the
     GPU forward, outside the timed region), timed on its own after the step.  Algorithmic
     FLOP: the usual 2.5x the forward's (five products per visible pair: S, dP, dV, dK,
     dQ); the kernels execute seven (S and dP are formed on both the dK/dV and the dQ
-    side), reported as executed_tflops."""
+    side), reported as executed_tflops.  With `power`, board power and clocks are then
+    sampled while the call repeats."""
     import torch
     print(f"[bench] backward on {pcfg.name}", file=sys.stderr, flush=True)
     q, k, v, do = W.backward_inputs(pcfg.B, pcfg.Hq, pcfg.Hkv, pcfg.Nq, pcfg.Nk, pcfg.d, seed=0,
@@ -364,17 +373,24 @@ def bench_backward(fa, W, pcfg, dev, K):
     avg = sum(ms) / K
     flops = 2.5 * pcfg.flops()
     tf = flops / (avg * 1e-3) / 1e12
-    return {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
-            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_call_ms": round(avg, 4),
-            "median_call_ms": round(sorted(ms)[K // 2], 4), "flop_per_call": flops,
-            "executed_tflops": round(tf * 7 / 5, 2), "workload": pcfg.workload,
-            "kernels": "prep (D, lse2) + dK/dV per 256 keys + dQ per 128 rows (one call)"}
+    res = {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
+           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_call_ms": round(avg, 4),
+           "median_call_ms": round(sorted(ms)[K // 2], 4), "flop_per_call": flops,
+           "executed_tflops": round(tf * 7 / 5, 2), "workload": pcfg.workload,
+           "kernels": "prep (D, lse2) + dK/dV per 256 keys + dQ per 128 rows (one call)"}
+    if power:
+        pw = power_leg(call, torch.cuda.synchronize, seconds=3.0)
+        if pw is not None:
+            pw["pj_per_flop"] = round(pw["socket_power_w_median"] / (tf * 1e12) * 1e12, 3)
+        res["power"] = pw
+    return res
 
 
-def bench_prefill_leg(fa, W, name, dev, launches, min_seconds=0.3):
+def bench_prefill_leg(fa, W, name, dev, launches, min_seconds=0.3, power=False):
     """Another prefill workload of the same kernel (the short MHA one, or the peaky 8K MHA
     one), timed on its own after the step: `launches` back-to-back launches, each between
-    two HIP events on the stream the kernel runs on; algorithmic TFLOP/s as for the step."""
+    two HIP events on the stream the kernel runs on; algorithmic TFLOP/s as for the step.
+    With `power`, board power and clocks are then sampled while the launch repeats."""
     import torch
     cfg = W.CONFIGS[name]
     print(f"[bench] prefill leg {name}", file=sys.stderr, flush=True)
@@ -405,11 +421,23 @@ def bench_prefill_leg(fa, W, name, dev, launches, min_seconds=0.3):
     avg = sum(ms) / launches
     flops = cfg.flops()
     tf = flops / (avg * 1e-3) / 1e12
-    return {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
-            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
-            "median_launch_ms": round(sorted(ms)[launches // 2], 4), "launches": launches,
-            "flop_per_launch": flops, "workload": cfg.workload,
-            "kernel": f"prefill_bf16_kernel<{cfg.d}, causal>"}
+    res = {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
+           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
+           "median_launch_ms": round(sorted(ms)[launches // 2], 4), "launches": launches,
+           "flop_per_launch": flops, "workload": cfg.workload,
+           "kernel": f"prefill_bf16_kernel<{cfg.d}, causal>"}
+    if power:
+        # launches grouped so that a group lasts at least ~0.5 ms between host syncs
+        group = max(1, int(math.ceil(0.5 / max(avg, 1e-3))))
+
+        def run_group():
+            for _ in range(group):
+                call()
+        pw = power_leg(run_group, torch.cuda.synchronize, seconds=3.0)
+        if pw is not None:
+            pw["pj_per_flop"] = round(pw["socket_power_w_median"] / (tf * 1e12) * 1e12, 3)
+        res["power"] = pw
+    return res
 
 
 def parse_smi_metric(text):
@@ -791,6 +819,11 @@ def main():
                                             "(kv_cache_empty)"}
         result["decode"]["separate_allocations"] = bench_decode_separate(fa, W, dcfg, dec, dev, K)
         if not args.no_power:
+            def decode_group():
+                for _ in range(8):
+                    decode()
+            pw = power_leg(decode_group, torch.cuda.synchronize, seconds=3.0)
+            result["decode"]["power"] = pw
             sc = stream_ceiling_leg(fa, dev, dbytes)
             sc["kernel_frac_of_ceiling"] = round(gbs / sc["value"], 4)
             result["decode"]["stream_ceiling"] = sc
@@ -805,17 +838,19 @@ def main():
         legs = {}
         for name, launches in (("c3", max(100, 5 * K)), ("c2", 1000)):
             if name != pcfg.name:
-                legs[name] = bench_prefill_leg(fa, W, name, dev, launches)
+                legs[name] = bench_prefill_leg(fa, W, name, dev, launches,
+                                               power=not args.no_power)
                 torch.cuda.empty_cache()
         result["prefill_legs"] = legs
     if not args.no_varlen:
         result["prefill_varlen"] = bench_varlen(fa, W, dev, K)
         torch.cuda.empty_cache()
     if not args.no_fp8:
-        result["prefill_fp8"] = bench_fp8(fa, W, pcfg, dev, K)
+        result["prefill_fp8"] = bench_fp8(fa, W, pcfg, dev, K, power=not args.no_power)
         torch.cuda.empty_cache()
     if not args.no_backward:
-        result["backward"] = bench_backward(fa, W, pcfg, dev, max(2, K // 4))
+        result["backward"] = bench_backward(fa, W, pcfg, dev, max(2, K // 4),
+                                            power=not args.no_power)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline_prefill(pcfg, args.cpu_seconds)
