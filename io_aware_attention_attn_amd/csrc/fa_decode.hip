@@ -489,6 +489,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int per_b = Hkv * QG;
+  const size_t row = (size_t)b * Hq + hq;
+  const float* pl = part_lse + row * max_pieces;
+  const float* po = part_o + row * max_pieces * D + lane * DPL;
+  // The first kSpec pieces of each wave (pieces wave, wave + NW, ...) are read before the
+  // piece count is known, so these reads overlap the length reads below.  Slots at or past
+  // the count (inside the workspace row) hold whatever earlier calls left there; they are
+  // dropped by the count test and never enter the arithmetic.
+  constexpr int kSpec = 4;
+  float lv[kSpec], ov[kSpec][DPL];
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const int ci = wave + u * NW;
+    lv[u] = kNegInf;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) ov[u][i] = 0.f;
+    if (ci < max_pieces) {
+      lv[u] = pl[ci];
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) ov[u][i] = po[(size_t)ci * D + i];
+    }
+  }
   auto nsteps = [&](int bb) {
     int L = seqlens[bb];
     L = L < 0 ? 0 : (L > Nk_max ? Nk_max : L);
@@ -522,36 +543,28 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   const int seg = (hq / G) * QG + (hq % G) / 16;
   const int S = base + seg * nb;
   const int nc = nb > 0 ? (S + nb - 1) / R - S / R + 1 : 0;
-  const size_t row = (size_t)b * Hq + hq;
-  const float* pl = part_lse + row * max_pieces;
-  const float* po = part_o + row * max_pieces * D + lane * DPL;
-
-  // Wave-level maximum over this wave's pieces (every lane reads the same lse values).
+  // Wave-level maximum and weighted sums over this wave's pieces (every lane reads the
+  // same lse values); pieces beyond the first kSpec per wave (long segments) are read here.
   float M = kNegInf;
-  for (int ci = wave; ci < nc; ci += NW) M = fmaxf(M, pl[ci]);
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u)
+    if (wave + u * NW < nc) M = fmaxf(M, lv[u]);
+  for (int ci = wave + kSpec * NW; ci < nc; ci += NW) M = fmaxf(M, pl[ci]);
   float ssum = 0.f;
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   const float Mref = (M == kNegInf) ? 0.f : M;
-  int ci = wave;
-  for (; ci + 3 * NW < nc; ci += 4 * NW) {  // four piece rows in flight
-    float lv[4], ov[4][DPL];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      lv[u] = pl[ci + u * NW];
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) ov[u][i] = po[(size_t)(ci + u * NW) * D + i];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kSpec; ++u) {
+    if (wave + u * NW < nc) {
       const float w = fast_exp2((lv[u] - Mref) * kLog2e);
       ssum += w;
 #pragma unroll
       for (int i = 0; i < DPL; ++i) acc[i] = fmaf(w, ov[u][i], acc[i]);
     }
   }
-  for (; ci < nc; ci += NW) {
+  for (int ci = wave + kSpec * NW; ci < nc; ci += NW) {
     const float w = fast_exp2((pl[ci] - Mref) * kLog2e);
     ssum += w;
 #pragma unroll
