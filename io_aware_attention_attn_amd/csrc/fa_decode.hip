@@ -515,31 +515,43 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     L = L < 0 ? 0 : (L > Nk_max ? Nk_max : L);
     return (L + 63) / 64;
   };
-  // T = all steps, pre = steps of the sequences before b
-  int tot = 0, pre = 0;
-  for (int bb = threadIdx.x; bb < B; bb += kMergeThreads) {
-    const int n = nsteps(bb) * per_b;
-    tot += n;
-    pre += (bb < b) ? n : 0;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    tot += __shfl_xor(tot, off);
-    pre += __shfl_xor(pre, off);
-  }
-  if (lane == 0) {
-    s_tot[wave] = tot;
-    s_pre[wave] = pre;
-  }
-  __syncthreads();
+  const int nb = nsteps(b);  // read now, beside the other lengths
+  // T = all steps, pre = steps of the sequences before b: with at most 64 sequences every
+  // wave sums the lengths itself (one per lane), otherwise the workgroup shares the sum
   int T = 0, base = 0;
+  if (B <= 64) {
+    const int n = lane < B ? nsteps(lane) * per_b : 0;
+    int tot = n, pre = lane < b ? n : 0;
+    for (int off = 32; off > 0; off >>= 1) {
+      tot += __shfl_xor(tot, off);
+      pre += __shfl_xor(pre, off);
+    }
+    T = tot;
+    base = pre;
+  } else {
+    int tot = 0, pre = 0;
+    for (int bb = threadIdx.x; bb < B; bb += kMergeThreads) {
+      const int n = nsteps(bb) * per_b;
+      tot += n;
+      pre += (bb < b) ? n : 0;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      tot += __shfl_xor(tot, off);
+      pre += __shfl_xor(pre, off);
+    }
+    if (lane == 0) {
+      s_tot[wave] = tot;
+      s_pre[wave] = pre;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    T += s_tot[i];
-    base += s_pre[i];
+    for (int i = 0; i < NW; ++i) {
+      T += s_tot[i];
+      base += s_pre[i];
+    }
   }
   const int R = steps_per_wave(T, W, rmin);
   const int G = Hq / Hkv;
-  const int nb = nsteps(b);
   const int seg = (hq / G) * QG + (hq % G) / 16;
   const int S = base + seg * nb;
   const int nc = nb > 0 ? (S + nb - 1) / R - S / R + 1 : 0;
