@@ -388,9 +388,12 @@ def bench_backward(fa, W, pcfg, dev, K, power=False):
 
 def bench_prefill_leg(fa, W, name, dev, launches, min_seconds=0.3, power=False):
     """Another prefill workload of the same kernel (the short MHA one, or the peaky 8K MHA
-    one), timed on its own after the step: `launches` back-to-back launches, each between
-    two HIP events on the stream the kernel runs on; algorithmic TFLOP/s as for the step.
-    With `power`, board power and clocks are then sampled while the launch repeats."""
+    one), timed on its own after the step: `launches` back-to-back launches in ten groups,
+    each group between two HIP events on the stream the kernel runs on, so the figure is the
+    kernels' own rate (an event pair around every launch of a 25 us kernel adds the events'
+    own few microseconds to each; that per-launch figure is reported beside it);
+    algorithmic TFLOP/s as for the step.  With `power`, board power and clocks are then
+    sampled while the launch repeats."""
     import torch
     cfg = W.CONFIGS[name]
     print(f"[bench] prefill leg {name}", file=sys.stderr, flush=True)
@@ -409,21 +412,37 @@ def bench_prefill_leg(fa, W, name, dev, launches, min_seconds=0.3, power=False):
         if n % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    groups = 10
+    per_group = max(1, launches // groups)
+    launches = groups * per_group
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(launches)]
+          for _ in range(groups)]
     for a, b in ev:
+        a.record()
+        for _ in range(per_group):
+            call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) / per_group for a, b in ev]
+    avg = sum(ms) / groups
+    # the same launches, each between its own pair of events
+    ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(launches, 200))]
+    for a, b in ev1:
         a.record()
         call()
         b.record()
     torch.cuda.synchronize()
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item(), "non-finite output"
-    ms = [a.elapsed_time(b) for a, b in ev]
-    avg = sum(ms) / launches
+    ms1 = sorted(a.elapsed_time(b) for a, b in ev1)
     flops = cfg.flops()
     tf = flops / (avg * 1e-3) / 1e12
     res = {"value": round(tf, 2), "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
-           "median_launch_ms": round(sorted(ms)[launches // 2], 4), "launches": launches,
+           "median_launch_ms": round(sorted(ms)[groups // 2], 4), "launches": launches,
+           "timing": f"{groups} groups of {per_group} back-to-back launches, one event pair "
+                     "per group",
+           "per_launch_event_median_ms": round(ms1[len(ms1) // 2], 4),
            "flop_per_launch": flops, "workload": cfg.workload,
            "kernel": f"prefill_bf16_kernel<{cfg.d}, causal>"}
     if power:

@@ -209,7 +209,7 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
   // this lane's share of the row sum of the fp32 weights, in two independent chains
   float ls_a = 0.f, ls_b = 0.f;
   float lim = kSumCap8;     // that sum after the last block, plus kSumCap8
-  const i32x8 ones = {kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3,
+  i32x8 ones = {kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3,
                       kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3};
 
   auto qk = [&](const uint8_t* kt, f32x16* s) __attribute__((always_inline)) {
@@ -367,6 +367,9 @@ prefill_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
   using S1 = std::integral_constant<int, 1>;
   int j = 0;
   for (; j + 2 < n; j += 2) {
+    // the block of ones stays in its eight registers across the loop (left to itself the
+    // compiler rebuilds it with seven v_mov before every row-sum product)
+    asm volatile("" : "+v"(ones));
     step_next(S0{}, j, s_a, s_b);
     step_next(S1{}, j + 1, s_b, s_a);
   }
