@@ -111,6 +111,25 @@ def test_c4_sampled():
              row_blocks=[(0, 256), (16320, 16450), (N - 256, N)])
 
 
+def test_c4_every_head_sampled_rows():
+    """Every one of c4's 64 query heads (so every GQA head-to-K/V-head pairing) at eight row
+    ranges of four rows spread over the whole sequence (first and last tiles, a 128-row tile
+    boundary, the middle, the ragged end of the causal span), against the oracle on that
+    head's slice."""
+    cfg = W.CONFIGS["c4"]
+    N, G = cfg.Nq, cfg.Hq // cfg.Hkv
+    q, k, v = W.prefill_inputs_for(cfg)
+    o, lse = _run_forward(q, k, v, cfg.scale, cfg.causal)
+    o, lse = o.cpu(), lse.cpu()
+    starts = (0, 60, 124, 8188, 16380, 24572, N - 132, N - 4)
+    for h in range(cfg.Hq):
+        qh, kh, vh = q[:, :, h:h + 1], k[:, :, h // G:h // G + 1], v[:, :, h // G:h // G + 1]
+        for r0 in starts:
+            o_ref, lse_ref = oracle.attention(qh, kh, vh, cfg.scale, cfg.causal, rows=(r0, r0 + 4))
+            _cmp(o[:, r0:r0 + 4, h], lse[:, h, r0:r0 + 4], o_ref[:, r0:r0 + 4, 0],
+                 lse_ref[:, 0, r0:r0 + 4], TOL_BF16, f"c4 head {h} rows {r0}:{r0 + 4}")
+
+
 def test_prefill_max_offsets():
     """The longest sequence the host accepts for Hq = 64, Hkv = 8, d = 128: one batch
     slice of O just under 2^31 bytes (N = 65279, odd, so the last tile is ragged).  Rows at
