@@ -556,6 +556,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  // -D of this lane's row in every accumulator register: the dP^T products start from it,
+  // so they end at dP - D with no subtraction per score
+  f32x16 negd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = -dd;
 
   // key tiles every row of the block sees in full (and that lie inside Nk) need no mask
   const int n_open =
@@ -579,7 +584,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const char* kt = reinterpret_cast<const char*>(ks(st));
     const char* vt = reinterpret_cast<const char*>(vs(st));
 
-    // per 32-key half: S^T = K Q^T and dP^T = V dO^T (lane = query row), then dS^T, then
+    // per 32-key half: S^T = K Q^T and dP^T - D = V dO^T - D (lane = query row), then dS^T, then
     // dQ^T += K^T dS^T; half 1's products overlap half 0's VALU work
     f32x16 s[2], dp[2];
     bf16x8 dsp[4];
@@ -587,7 +592,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                            : Nk - 1 - j * kTile - 4 * hi;
     auto sdp = [&](int kb) __attribute__((always_inline)) {
       s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      dp[kb] = negd;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         const int row = 32 * kb + l32;
@@ -611,7 +616,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const int kl = kb * 32 + 8 * (r >> 2) + (r & 3);
             float p = fast_exp2(fmaf(s[kb][r], c, -l2));
             if (masked) p = (kl <= lim) ? p : 0.f;
-            v2[e] = p * (dp[kb][r] - dd);
+            v2[e] = p * dp[kb][r];  // P (dP - D)
           }
           w[t] = pack_bf16x2(v2[0], v2[1]);
         }
